@@ -1,0 +1,15 @@
+"""Focus oracle (test infrastructure only; see focus_ref's header)."""
+from .focus_ref import (  # noqa: F401
+    TIE_LOG,
+    TIE_REL,
+    allowed_keys_ref,
+    assign_ref,
+    attention_rows_ref,
+    decode_ref,
+    owner_ref,
+    pair_count_ref,
+    scores_ref,
+    sinkhorn_ref,
+    soft_gate_ref,
+    topk_ref,
+)
