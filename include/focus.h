@@ -1,0 +1,194 @@
+/*
+ * focus.h - C ABI of the Focus inference path on AMD Instinct MI355X (gfx950).
+ *
+ * Focus ("Why Attend to Everything? Focus is the Key", arXiv 2604.03260) gates causal
+ * attention with K learned centroids: hidden states are projected into a small group space,
+ * scored against the centroids, balanced with Sinkhorn normalisation and given hard top-k
+ * group membership; query i then attends key j <= i only if |i - j| < window or the two
+ * tokens share at least one group, with an exact softmax over the allowed pairs.
+ *
+ * Pages cited below:
+ *   (ZH)  "Why Attend to Everything? Focus is the Key", Chinese technical summary
+ *         (gist.science/zh), sections 2.1.1 token grouping, 2.1.2 gated attention,
+ *         2.1.3 top-k inference.
+ *   (NL)  Same title, Dutch technical summary (gist.science/nl), "Kerncomponenten" 1-4.
+ *   (ABS) Same title, English abstract (arxivdaily.com).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device buffers are device memory of the current HIP device, owned by
+ *     the caller; the library never allocates, frees or retains them and keeps no state
+ *     between calls. Scratch memory comes from the caller as `workspace`, sized by the
+ *     matching *_workspace_size query.
+ *   - bf16 tensors, the fp32 inputs of focus_assign and every workspace must be 16-byte
+ *     aligned; int32 buffers and fp32 lse / col_potential outputs 4-byte aligned (else
+ *     FOCUS_ERR_ALIGN). Tensors are dense and row-major in the shapes given. bf16 tensors are
+ *     passed as uint16_t bit patterns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without waiting. Inputs are never written. Calls are re-entrant; two calls
+ *     that share a workspace must not overlap in time.
+ *   - Arguments are validated on the host before anything is enqueued; an invalid call
+ *     returns a negative status and enqueues nothing. A failed launch returns FOCUS_ERR_HIP.
+ *     No C++ exception crosses this interface.
+ *   - Index tensors are int32: n * top_k (tokens times memberships) must be below 2^31.
+ */
+#ifndef FOCUS_H
+#define FOCUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum focus_status {
+  FOCUS_OK = 0,
+  FOCUS_ERR_ARG = -1,          /* NULL pointer or out-of-range scalar argument          */
+  FOCUS_ERR_SHAPE = -2,        /* sizes that overflow the int32 index space              */
+  FOCUS_ERR_UNSUPPORTED = -3,  /* a valid shape this build has no kernel for             */
+  FOCUS_ERR_ALIGN = -4,        /* a device pointer that is not 16-byte aligned           */
+  FOCUS_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than the size query returns  */
+  FOCUS_ERR_HIP = -6           /* the HIP runtime reported an error while enqueueing     */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* focus_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int focus_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * focus_assign - centroid group assignment (ZH 2.1.1 and 2.1.3; NL Kerncomponenten 1, 2, 4).
+ *
+ *   S = (hidden * w_g) * centroids^T                     scores, [n, K], fp32 arithmetic
+ *   repeat sinkhorn_iters times (log domain, unit temperature, u = v = 0 at the start):
+ *     u_i = -logsumexp_c (S_ic + v_c)                    every token carries mass 1
+ *     v_c = log(n / K) - logsumexp_i (S_ic + u_i)        every group receives mass n / K
+ *   groups[i] = the top_k groups c with the largest S_ic + v_c (equal scores: lower c first),
+ *               written in ascending group order.
+ *
+ *   hidden        device, [n, d] fp32, d % 4 == 0.
+ *   w_g           device, [d, d_g] fp32 projection into group space, d_g % 4 == 0.
+ *   centroids     device, [K, d_g] fp32.
+ *   n             tokens, n >= 0 (n == 0: nothing is enqueued, outputs untouched).
+ *   d, d_g        1 <= d, 1 <= d_g <= 1024.
+ *   K             number of groups, 1 <= K <= 1024.
+ *   top_k         memberships per token, 1 <= top_k <= min(K, 8).
+ *   sinkhorn_iters  >= 0; 0 ranks the raw scores.
+ *   groups        device, out [n, top_k] int32, distinct group ids in [0, K), ascending.
+ *   col_potential device, out [K] fp32, the column potential v after the last iteration;
+ *                 may be NULL.
+ *   workspace     device scratch of at least focus_assign_workspace_size(n, d, d_g, K) bytes.
+ * ------------------------------------------------------------------------------------ */
+size_t focus_assign_workspace_size(int64_t n, int d, int d_g, int K);
+int focus_assign(const float* hidden, const float* w_g, const float* centroids,
+                 int64_t n, int d, int d_g, int K, int top_k, int sinkhorn_iters,
+                 int32_t* groups, float* col_potential,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * focus_bucket - stable counting sort of memberships into per-group segments
+ * (the membership sets of ZH 2.1.3, laid out so each group's tokens are contiguous).
+ *
+ * For each of `batch` independent sequences of n tokens:
+ *   offsets[b, c]  = number of memberships with a group id below c (offsets[b, K] = total),
+ *   idx[b, s]      = token position of membership slot s; inside every segment
+ *                    [offsets[b,c], offsets[b,c+1]) positions are strictly ascending,
+ *   slot[b, i, r]  = the slot s holding membership (i, groups[b, i, r]).
+ * A membership whose group id lies outside [0, K) is dropped: its slot is -1 and it appears
+ * in no segment. Group ids of one token must be distinct.
+ *
+ *   groups   device, [batch, n, top_k] int32.
+ *   batch    >= 1; n >= 0; 1 <= K <= 1024; 1 <= top_k <= 8.
+ *   offsets  device, out [batch, K + 1] int32.
+ *   idx      device, out [batch, n * top_k] int32 (entries past offsets[b, K] are -1).
+ *   slot     device, out [batch, n, top_k] int32.
+ *   workspace  at least focus_bucket_workspace_size(batch, n, K, top_k) bytes.
+ * ------------------------------------------------------------------------------------ */
+size_t focus_bucket_workspace_size(int batch, int64_t n, int K, int top_k);
+int focus_bucket(const int32_t* groups, int batch, int64_t n, int K, int top_k,
+                 int32_t* offsets, int32_t* idx, int32_t* slot,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * focus_attention - gated sparse causal attention for one sequence
+ * (ZH 2.1.2 and 2.1.3; NL Kerncomponenten 3; ABS).
+ *
+ *   allowed(i, j) = j <= i and (i - j < window or groups[i] and groups[j] share a group)
+ *   out[i, h]  = sum over allowed j of softmax_j(scale * q[i,h] . k[j,h/G]) * v[j,h/G]
+ *   lse[i, h]  = natural log of sum over allowed j of exp(scale * q[i,h] . k[j,h/G])
+ * with G = Hq / Hkv (query head h reads kv head h / G). Every allowed pair is counted once:
+ * the kernels split the pairs into the window (i - j < window) and, for far pairs, the
+ * lowest group the two tokens share, and merge the parts by their log-sum-exp.
+ *
+ *   q        device, [n, Hq, d_head] bf16;  k, v  device, [n, Hkv, d_head] bf16.
+ *   n        >= 0 (0: nothing enqueued). Hq % Hkv == 0 and G in {1, 2, 4, 8, 16}.
+ *   d_head   64 or 128.
+ *   groups   device, [n, top_k] int32, ascending distinct ids in [0, K) (focus_assign output).
+ *   offsets, idx, slot   device, focus_bucket output for these groups (batch 1).
+ *   K        1 <= K <= 1024; top_k 1 <= top_k <= min(K, 4).
+ *   window   >= 0 (0: only pairs that share a group, the diagonal included).
+ *   scale    > 0, or <= 0 for 1 / sqrt(d_head).
+ *   out      device, out [n, Hq, d_head] bf16.
+ *   lse      device, out [n, Hq] fp32.
+ *   workspace  at least focus_attention_workspace_size(n, Hq, Hkv, d_head, K, top_k) bytes.
+ * ------------------------------------------------------------------------------------ */
+size_t focus_attention_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K, int top_k);
+int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    int64_t n, int Hq, int Hkv, int d_head,
+                    const int32_t* groups, const int32_t* offsets, const int32_t* idx,
+                    const int32_t* slot, int K, int top_k, int64_t window, float scale,
+                    uint16_t* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as focus_attention, and in addition records caller-created hipEvent_t handles on
+ * `stream` around each of its five kernels, for benchmarks that time one stage:
+ * stage_events[2 s] just before and stage_events[2 s + 1] just after stage s, with
+ * s = 0 gather of Q/K/V into group segments, 1 tile prefix, 2 group attention,
+ * 3 window attention, 4 log-sum-exp merge. NULL entries are skipped; num_events is the
+ * length of the array (0 to 10). Event-record failures return FOCUS_ERR_HIP. */
+int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       int64_t n, int Hq, int Hkv, int d_head,
+                       const int32_t* groups, const int32_t* offsets, const int32_t* idx,
+                       const int32_t* slot, int K, int top_k, int64_t window, float scale,
+                       uint16_t* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* stage_events, int num_events);
+
+/* ------------------------------------------------------------------------------------
+ * focus_decode - one new token per sequence against its own cache (ZH 2.1.3 inference).
+ *
+ * Sequence b holds L_b = cache_len[b] tokens; its new token is the last one, at position
+ * L_b - 1, whose K/V the caller has already written to the caches. The query carries the
+ * groups q_groups[b] and attends key j <= L_b - 1 when L_b - 1 - j < window or when
+ * cache_groups[b, j] shares a group with q_groups[b]; the new token always attends itself.
+ * Results equal the last row of focus_attention over that sequence with groups[L_b - 1]
+ * replaced by q_groups[b].
+ *
+ *   q            device, [B, Hq, d_head] bf16.
+ *   q_groups     device, [B, top_k] int32.
+ *   k_cache, v_cache   device, [B, Lmax, Hkv, d_head] bf16.
+ *   cache_len    device, [B] int32, 1 <= cache_len[b] <= Lmax (values outside are clamped).
+ *   cache_groups device, [B, Lmax, top_k] int32.
+ *   cache_offsets, cache_idx   device, focus_bucket output over cache_groups with
+ *                batch = B and n = Lmax ([B, K + 1] and [B, Lmax * top_k]); tokens at
+ *                positions >= cache_len[b] are ignored.
+ *   B >= 0, Lmax >= 1, Lmax * top_k < 2^31; head, K and top_k limits as focus_attention.
+ *   out          device, out [B, Hq, d_head] bf16;  lse  device, out [B, Hq] fp32.
+ *   workspace    at least focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k).
+ * ------------------------------------------------------------------------------------ */
+size_t focus_decode_workspace_size(int B, int64_t Lmax, int Hq, int Hkv, int d_head, int K,
+                                   int top_k);
+int focus_decode(const uint16_t* q, const int32_t* q_groups,
+                 const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cache_len,
+                 const int32_t* cache_groups, const int32_t* cache_offsets,
+                 const int32_t* cache_idx, int B, int64_t Lmax, int Hq, int Hkv, int d_head,
+                 int K, int top_k, int64_t window, float scale,
+                 uint16_t* out, float* lse,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOCUS_H */

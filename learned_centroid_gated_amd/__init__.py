@@ -1,0 +1,16 @@
+"""Focus (learned centroid-gated sparse attention) inference path for AMD MI355X (gfx950).
+
+The compute lives in libfocus.so (hand-written HIP kernels behind the C ABI of
+include/focus.h); this package only marshals arguments to it.
+"""
+from .focus import (  # noqa: F401
+    focus_assign,
+    focus_assign_workspace_size,
+    focus_attention,
+    focus_attention_workspace_size,
+    focus_bucket,
+    focus_bucket_workspace_size,
+    focus_decode,
+    focus_decode_workspace_size,
+)
+from ._lib import LIB_PATH, FocusError, lib, status_string  # noqa: F401

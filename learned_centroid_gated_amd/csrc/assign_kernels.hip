@@ -1,0 +1,418 @@
+// Centroid group assignment on gfx950: scores S = (H W_g) C^T on fp32 MFMA, log-domain
+// Sinkhorn balancing and top-k membership.
+//
+// Method: "Why Attend to Everything? Focus is the Key" (Chinese technical summary,
+// gist.science/zh, section 2.1.1: projection into centroid space, similarity to K centroids,
+// Sinkhorn in place of softmax so each group gets equal token mass; section 2.1.3: each token
+// joins its k highest-scoring groups at inference).
+#include "focus_internal.hpp"
+
+namespace focus {
+
+// ============================================================================ fp32 NT GEMM
+// C[m, n] = sum_k A[m, k] * B[n, k]. Block tile 128 x (32*NT), k-chunks of 32 staged in LDS.
+// Each wave owns 32 rows and NT 32x32 accumulator tiles of v_mfma_f32_32x32x2_f32.
+// In a k-chunk, lane half g (lanes 32g..32g+31) supplies contraction indices 16g..16g+15,
+// one per MFMA step, so each lane reads 16 contiguous floats of its A row and B row with
+// four 16-byte LDS loads; the same index map on both operands keeps the sum exact.
+template <int NT>
+__global__ __launch_bounds__(256) void gemm_nt_f32_kernel(const float* __restrict__ A,
+                                                          const float* __restrict__ B,
+                                                          float* __restrict__ C, int64_t M, int N,
+                                                          int Kd, int ldc) {
+  constexpr int BM = 128, BN = 32 * NT, BK = 32, LDP = BK + 4;
+  __shared__ __attribute__((aligned(16))) float As[BM * LDP];
+  __shared__ __attribute__((aligned(16))) float Bs[BN * LDP];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, j = l & 31, g = l >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16_t{};
+
+  f32x4_t ra[4], rb[NT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
+      int64_t gr = m0 + r;
+      ra[i] = (gr < M && k0 + c < Kd) ? *(const f32x4_t*)(A + gr * Kd + k0 + c) : f32x4_t{};
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
+      int gr = n0 + r;
+      rb[i] = (gr < N && k0 + c < Kd) ? *(const f32x4_t*)(B + (int64_t)gr * Kd + k0 + c) : f32x4_t{};
+    }
+  };
+
+  load(0);
+  for (int k0 = 0; k0 < Kd; k0 += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
+      *(f32x4_t*)&As[r * LDP + c] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
+      *(f32x4_t*)&Bs[r * LDP + c] = rb[i];
+    }
+    __syncthreads();
+    if (k0 + BK < Kd) load(k0 + BK);
+
+    f32x4_t a4[4];
+    const float* ap = &As[(wave * 32 + j) * LDP + 16 * g];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a4[q] = *(const f32x4_t*)(ap + 4 * q);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f32x4_t b4[4];
+      const float* bp = &Bs[(t * 32 + j) * LDP + 16 * g];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b4[q] = *(const f32x4_t*)(bp + 4 * q);
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[s >> 2][s & 3], b4[s >> 2][s & 3], acc[t],
+                                                      0, 0, 0);
+    }
+  }
+
+  // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int col = n0 + t * 32 + j;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int64_t row = m0 + wave * 32 + (v >> 2) * 8 + 4 * g + (v & 3);
+      if (row < M && col < N) C[row * ldc + col] = acc[t][v];
+    }
+  }
+}
+
+hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int64_t M, int N, int Kd,
+                              int ldc, hipStream_t stream) {
+  dim3 block(256);
+  int64_t mb = (M + 127) / 128;
+  if (N <= 32) {
+    hipLaunchKernelGGL(gemm_nt_f32_kernel<1>, dim3(mb, (N + 31) / 32), block, 0, stream, A, B, C, M,
+                       N, Kd, ldc);
+  } else if (N <= 64) {
+    hipLaunchKernelGGL(gemm_nt_f32_kernel<2>, dim3(mb, (N + 63) / 64), block, 0, stream, A, B, C, M,
+                       N, Kd, ldc);
+  } else {
+    hipLaunchKernelGGL(gemm_nt_f32_kernel<4>, dim3(mb, (N + 127) / 128), block, 0, stream, A, B, C,
+                       M, N, Kd, ldc);
+  }
+  return hipGetLastError();
+}
+
+// ============================================================================ transpose
+__global__ __launch_bounds__(256) void transpose_f32_kernel(const float* __restrict__ B,
+                                                            float* __restrict__ Bt, int R, int Cn) {
+  __shared__ float tile[32][33];
+  int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int y = ty; y < 32; y += 8)
+    if (r0 + y < R && c0 + tx < Cn) tile[y][tx] = B[(int64_t)(r0 + y) * Cn + c0 + tx];
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8)
+    if (c0 + y < Cn && r0 + tx < R) Bt[(int64_t)(c0 + y) * R + r0 + tx] = tile[tx][y];
+}
+
+hipError_t launch_transpose_f32(const float* B, float* Bt, int Kd, int N, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_f32_kernel, dim3((N + 31) / 32, (Kd + 31) / 32), dim3(256), 0,
+                     stream, B, Bt, Kd, N);
+  return hipGetLastError();
+}
+
+__global__ void fill_f32_kernel(float* p, float value, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+hipError_t launch_fill_f32(float* p, float value, int64_t count, hipStream_t stream) {
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, stream, p, value, count);
+  return hipGetLastError();
+}
+
+// ============================================================================ row layouts
+// A row of K scores is spread over LPR lanes; lane q of the row holds columns
+// 4q + 4*LPR*c + e (c < CPL, e < 4). Rows per wave: 64 / LPR.
+template <int LPR>
+__device__ __forceinline__ float row_max(float x) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) x = fmaxf(x, shfl_xor_f(x, o));
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) x += shfl_xor_f(x, o);
+  return x;
+}
+
+// Merge two (max, sum) summaries of exp: sum_i exp(x_i) = exp(m) * s.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * fast_exp2((m - M) * kLog2e) + s2 * fast_exp2((m2 - M) * kLog2e);
+  m = M;
+}
+
+// ============================================================================ Sinkhorn pass
+// Row step u_i = -logsumexp_c(S_ic + v_c) for the block's rows, and the block's summary of
+// sum_i exp(S_ic + u_i) for every column c as a (max, sum) pair.
+template <int LPR, int CPL>
+__global__ __launch_bounds__(256) void sinkhorn_rows_kernel(const float* __restrict__ S, int64_t n,
+                                                            int K, int ldS,
+                                                            const float* __restrict__ v,
+                                                            float2* __restrict__ partials,
+                                                            int64_t rows_per_block) {
+  constexpr int RPW = kWave / LPR;
+  constexpr int NC = 4 * CPL;
+  __shared__ float2 red[4][NC * LPR];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, q = l % LPR, rg = l / LPR;
+  const int64_t r_begin = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t r_end = r_begin + rows_per_block < n ? r_begin + rows_per_block : n;
+
+  float vv[NC];
+  bool ok[NC];
+  float cm[NC], cs[NC];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int col = 4 * q + 4 * LPR * c + e;
+      ok[4 * c + e] = col < K;
+      vv[4 * c + e] = col < K ? v[col] : 0.f;
+      cm[4 * c + e] = -INFINITY;
+      cs[4 * c + e] = 0.f;
+    }
+
+  for (int64_t row = r_begin + wave * RPW + rg; row < r_end; row += 4 * RPW) {
+    float s[NC];
+    const float* sp = S + row * ldS;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      int col = 4 * q + 4 * LPR * c;
+      f32x4_t x = col < K ? *(const f32x4_t*)(sp + col) : f32x4_t{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * c + e] = x[e];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (ok[i]) mx = fmaxf(mx, s[i] + vv[i]);
+    mx = row_max<LPR>(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (ok[i]) sum += fast_exp2((s[i] + vv[i] - mx) * kLog2e);
+    sum = row_sum<LPR>(sum);
+    const float u = -(mx + __logf(sum));
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (!ok[i]) continue;
+      float x = s[i] + u;
+      float d = x - cm[i];
+      float e = fast_exp2(-fabsf(d) * kLog2e);
+      if (d > 0.f) {
+        cs[i] = cs[i] * e + 1.f;
+        cm[i] = x;
+      } else {
+        cs[i] += e;
+      }
+    }
+  }
+  // combine the row groups of the wave (lanes with equal q)
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      float m2 = shfl_xor_f(cm[i], o), s2 = shfl_xor_f(cs[i], o);
+      ms_merge(cm[i], cs[i], m2, s2);
+    }
+  if (rg == 0) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) red[wave][i * LPR + q] = make_float2(cm[i], cs[i]);
+  }
+  __syncthreads();
+  for (int t = tid; t < NC * LPR; t += 256) {
+    int i = t / LPR, qq = t % LPR;
+    int col = 4 * qq + 4 * LPR * (i / 4) + (i % 4);
+    if (col >= K) continue;
+    float m = red[0][t].x, s = red[0][t].y;
+    for (int w = 1; w < 4; ++w) ms_merge(m, s, red[w][t].x, red[w][t].y);
+    partials[(int64_t)blockIdx.x * K + col] = make_float2(m, s);
+  }
+}
+
+// Column step: v_c = log(n / K) - logsumexp_i(S_ic + u_i), from the block summaries (fp64).
+__global__ __launch_bounds__(256) void sinkhorn_cols_kernel(const float2* __restrict__ partials,
+                                                            int nblocks, int K, double log_mass,
+                                                            float* __restrict__ v) {
+  __shared__ double sm[256], ss[256];
+  const int c = blockIdx.x, t = threadIdx.x;
+  double m = -INFINITY, s = 0.0;
+  for (int b = t; b < nblocks; b += 256) {
+    float2 p = partials[(int64_t)b * K + c];
+    double pm = p.x, ps = p.y;
+    double M = m > pm ? m : pm;
+    if (M == -INFINITY) continue;
+    s = s * exp(m - M) + ps * exp(pm - M);
+    m = M;
+  }
+  sm[t] = m;
+  ss[t] = s;
+  __syncthreads();
+  for (int o = 128; o >= 1; o >>= 1) {
+    if (t < o) {
+      double m1 = sm[t], m2 = sm[t + o];
+      double M = m1 > m2 ? m1 : m2;
+      if (M != -INFINITY) {
+        ss[t] = ss[t] * exp(m1 - M) + ss[t + o] * exp(m2 - M);
+        sm[t] = M;
+      }
+    }
+    __syncthreads();
+  }
+  if (t == 0) v[c] = (float)(log_mass - (sm[0] + log(ss[0])));
+}
+
+int sinkhorn_blocks(int64_t n, int K) {
+  (void)K;
+  int64_t b = (n + 255) / 256;
+  if (b > 4096) b = 4096;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+template <int LPR, int CPL>
+static hipError_t sinkhorn_rows(const float* S, int64_t n, int K, int ldS, const float* v,
+                                float2* partials, int nblocks, hipStream_t stream) {
+  constexpr int gran = 4 * (kWave / LPR);
+  int64_t rpb = (n + nblocks - 1) / nblocks;
+  rpb = (rpb + gran - 1) / gran * gran;
+  hipLaunchKernelGGL((sinkhorn_rows_kernel<LPR, CPL>), dim3(nblocks), dim3(256), 0, stream, S, n,
+                     K, ldS, v, partials, rpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn_iter(const float* S, int64_t n, int K, int ldS, float* v,
+                                float2* partials, int nblocks, hipStream_t stream) {
+  hipError_t e;
+  if (K <= 16) e = sinkhorn_rows<4, 1>(S, n, K, ldS, v, partials, nblocks, stream);
+  else if (K <= 64) e = sinkhorn_rows<16, 1>(S, n, K, ldS, v, partials, nblocks, stream);
+  else if (K <= 256) e = sinkhorn_rows<64, 1>(S, n, K, ldS, v, partials, nblocks, stream);
+  else if (K <= 512) e = sinkhorn_rows<64, 2>(S, n, K, ldS, v, partials, nblocks, stream);
+  else e = sinkhorn_rows<64, 4>(S, n, K, ldS, v, partials, nblocks, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sinkhorn_cols_kernel, dim3(K), dim3(256), 0, stream, partials, nblocks, K,
+                     log((double)n / (double)K), v);
+  return hipGetLastError();
+}
+
+// ============================================================================ top-k
+// groups[i] = the top_k columns of S_i + v (equal values: lower column first), ascending.
+constexpr int kNone = 0x7fffffff;
+
+__device__ __forceinline__ bool better(float v2, int i2, float v1, int i1) {
+  if (i2 == kNone) return false;
+  if (i1 == kNone) return true;
+  return v2 > v1 || (v2 == v1 && i2 < i1);
+}
+
+template <int LPR, int CPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S,
+                                                   const float* __restrict__ v, int64_t n, int K,
+                                                   int ldS, int top_k,
+                                                   int32_t* __restrict__ groups) {
+  constexpr int RPW = kWave / LPR;
+  constexpr int NC = 4 * CPL;
+  const int l = threadIdx.x & 63, wave = threadIdx.x >> 6, q = l % LPR, rg = l / LPR;
+  float vv[NC];
+  int colx[NC];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int col = 4 * q + 4 * LPR * c + e;
+      colx[4 * c + e] = col < K ? col : kNone;
+      vv[4 * c + e] = col < K ? v[col] : 0.f;
+    }
+  const int64_t rows_per_block = 4 * RPW;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_block + wave * RPW + rg;
+  if (row >= n) return;  // a whole row group leaves together; shuffles stay within it
+  float b[NC];
+  const float* sp = S + row * ldS;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    int col = 4 * q + 4 * LPR * c;
+    f32x4_t x = col < K ? *(const f32x4_t*)(sp + col) : f32x4_t{};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[4 * c + e] = x[e] + vv[4 * c + e];
+  }
+  unsigned taken = 0;
+  int sel[8];
+  for (int r = 0; r < top_k; ++r) {
+    float bv = 0.f;
+    int bi = kNone;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (!((taken >> i) & 1u) && better(b[i], colx[i], bv, bi)) {
+        bv = b[i];
+        bi = colx[i];
+      }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) {
+      float v2 = shfl_xor_f(bv, o);
+      int i2 = shfl_xor_i(bi, o);
+      if (better(v2, i2, bv, bi)) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    sel[r] = bi;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (colx[i] == bi) taken |= 1u << i;
+  }
+  // ascending order of the selected set
+  for (int a = 1; a < top_k; ++a) {
+    int x = sel[a], p = a - 1;
+    while (p >= 0 && sel[p] > x) {
+      sel[p + 1] = sel[p];
+      --p;
+    }
+    sel[p + 1] = x;
+  }
+  if (q == 0)
+    for (int r = 0; r < top_k; ++r) groups[row * top_k + r] = sel[r];
+}
+
+template <int LPR, int CPL>
+static hipError_t topk_launch(const float* S, const float* v, int64_t n, int K, int ldS, int top_k,
+                              int32_t* groups, hipStream_t stream) {
+  int64_t rpb = 4 * (kWave / LPR);
+  hipLaunchKernelGGL((topk_kernel<LPR, CPL>), dim3((n + rpb - 1) / rpb), dim3(256), 0, stream, S, v,
+                     n, K, ldS, top_k, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* S, const float* v, int64_t n, int K, int ldS, int top_k,
+                       int32_t* groups, hipStream_t stream) {
+  if (K <= 16) return topk_launch<4, 1>(S, v, n, K, ldS, top_k, groups, stream);
+  if (K <= 64) return topk_launch<16, 1>(S, v, n, K, ldS, top_k, groups, stream);
+  if (K <= 256) return topk_launch<64, 1>(S, v, n, K, ldS, top_k, groups, stream);
+  if (K <= 512) return topk_launch<64, 2>(S, v, n, K, ldS, top_k, groups, stream);
+  return topk_launch<64, 4>(S, v, n, K, ldS, top_k, groups, stream);
+}
+
+}  // namespace focus

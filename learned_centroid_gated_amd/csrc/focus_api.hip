@@ -1,0 +1,339 @@
+// C ABI of the Focus library: host-side validation, workspace carving and launch order.
+// Every argument is checked before anything is enqueued, so invalid calls are testable on a
+// host without a GPU; no HIP call is made on an error path.
+#include <math.h>
+
+#include "../../include/focus.h"
+#include "focus_internal.hpp"
+
+using namespace focus;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kIdxLimit = (int64_t)1 << 31;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Carves consecutive 256-byte aligned regions out of a workspace (or only counts them).
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + used) : nullptr;
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? FOCUS_OK : FOCUS_ERR_HIP; }
+
+bool is_pow2_upto16(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// ------------------------------------------------------------------ assign plan
+// The scores are either two products (H W_g, then Z C^T) or one product against the folded
+// matrix W_g C^T, whichever needs fewer flops per token.
+bool assign_folds(int d, int d_g, int K) {
+  return (int64_t)d * K <= (int64_t)d * d_g + (int64_t)d_g * K;
+}
+inline int padded_k(int K) { return (K + 3) / 4 * 4; }
+
+struct AssignWs {
+  float* S;
+  float* Z;
+  float* Bt;
+  float* v;
+  float2* partials;
+};
+
+size_t assign_carve(void* ws, int64_t n, int d, int d_g, int K, AssignWs* out) {
+  Carver c(ws);
+  const bool fold = assign_folds(d, d_g, K);
+  AssignWs w{};
+  w.S = c.take<float>((size_t)n * padded_k(K));
+  w.Z = fold ? nullptr : c.take<float>((size_t)n * d_g);
+  w.Bt = c.take<float>((size_t)(fold ? K : d_g) * d);
+  w.v = c.take<float>((size_t)padded_k(K));
+  w.partials = c.take<float2>((size_t)sinkhorn_blocks(n, K) * K);
+  if (out) *out = w;
+  return c.used;
+}
+
+// ------------------------------------------------------------------ attention plan
+struct AttnWs {
+  uint16_t *qg, *kg, *vg;
+  float *og, *lseg, *ol, *lsel;
+  int32_t* tile_pre;
+};
+
+size_t attn_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k, AttnWs* out) {
+  Carver c(ws);
+  const int64_t nk = n * top_k;
+  AttnWs w{};
+  w.qg = c.take<uint16_t>((size_t)nk * Hq * dh);
+  w.kg = c.take<uint16_t>((size_t)nk * Hkv * dh);
+  w.vg = c.take<uint16_t>((size_t)nk * Hkv * dh);
+  w.og = c.take<float>((size_t)nk * Hq * dh);
+  w.lseg = c.take<float>((size_t)nk * Hq);
+  w.ol = c.take<float>((size_t)n * Hq * dh);
+  w.lsel = c.take<float>((size_t)n * Hq);
+  w.tile_pre = c.take<int32_t>((size_t)K + 1);
+  if (out) *out = w;
+  return c.used;
+}
+
+int check_heads(int Hq, int Hkv, int d_head) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FOCUS_ERR_ARG;
+  if (!is_pow2_upto16(Hq / Hkv)) return FOCUS_ERR_UNSUPPORTED;
+  if (d_head != 64 && d_head != 128) return FOCUS_ERR_UNSUPPORTED;
+  return FOCUS_OK;
+}
+
+int check_groups(int K, int top_k, int max_top_k) {
+  if (K < 1 || K > 1024) return FOCUS_ERR_ARG;
+  if (top_k < 1 || top_k > K) return FOCUS_ERR_ARG;
+  if (top_k > max_top_k) return FOCUS_ERR_UNSUPPORTED;
+  return FOCUS_OK;
+}
+
+int resolve_scale(float scale, int d_head, float* out) {
+  if (isnan(scale) || isinf(scale)) return FOCUS_ERR_ARG;
+  *out = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d_head));
+  return FOCUS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* focus_status_string(int status) {
+  switch (status) {
+    case FOCUS_OK: return "FOCUS_OK";
+    case FOCUS_ERR_ARG: return "FOCUS_ERR_ARG: null pointer or out-of-range argument";
+    case FOCUS_ERR_SHAPE: return "FOCUS_ERR_SHAPE: sizes overflow the int32 index space";
+    case FOCUS_ERR_UNSUPPORTED: return "FOCUS_ERR_UNSUPPORTED: shape has no kernel in this build";
+    case FOCUS_ERR_ALIGN: return "FOCUS_ERR_ALIGN: device pointer not 16-byte aligned";
+    case FOCUS_ERR_WORKSPACE: return "FOCUS_ERR_WORKSPACE: workspace missing or too small";
+    case FOCUS_ERR_HIP: return "FOCUS_ERR_HIP: HIP runtime error while enqueueing";
+    default: return "FOCUS_ERR_UNKNOWN";
+  }
+}
+
+int focus_version(void) { return 100; }  // 0.1.0
+
+// ============================================================================ assign
+size_t focus_assign_workspace_size(int64_t n, int d, int d_g, int K) {
+  if (n < 0 || d < 1 || d_g < 1 || K < 1) return 0;
+  return assign_carve(nullptr, n, d, d_g, K, nullptr);
+}
+
+int focus_assign(const float* hidden, const float* w_g, const float* centroids, int64_t n, int d,
+                 int d_g, int K, int top_k, int sinkhorn_iters, int32_t* groups,
+                 float* col_potential, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || d < 1 || d_g < 1 || d_g > 1024 || sinkhorn_iters < 0) return FOCUS_ERR_ARG;
+  if (d % 4 != 0 || d_g % 4 != 0) return FOCUS_ERR_UNSUPPORTED;
+  if (int st = check_groups(K, top_k, 8)) return st;
+  if (n * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (n == 0) return FOCUS_OK;
+  if (!hidden || !w_g || !centroids || !groups) return FOCUS_ERR_ARG;
+  if (!aligned16(hidden) || !aligned16(w_g) || !aligned16(centroids) || !aligned4(groups) ||
+      !aligned4(col_potential) || !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  AssignWs w;
+  const size_t need = assign_carve(workspace, n, d, d_g, K, &w);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int ldS = padded_k(K);
+  hipError_t e;
+  if (assign_folds(d, d_g, K)) {
+    // Bt = (W_g C^T)^T = C W_g^T  [K, d];  S = H Bt^T
+    e = launch_gemm_nt_f32(centroids, w_g, w.Bt, K, d, d_g, d, st);
+    if (e == hipSuccess) e = launch_gemm_nt_f32(hidden, w.Bt, w.S, n, K, d, ldS, st);
+  } else {
+    // Bt = W_g^T [d_g, d];  Z = H W_g;  S = Z C^T
+    e = launch_transpose_f32(w_g, w.Bt, d, d_g, st);
+    if (e == hipSuccess) e = launch_gemm_nt_f32(hidden, w.Bt, w.Z, n, d_g, d, d_g, st);
+    if (e == hipSuccess) e = launch_gemm_nt_f32(w.Z, centroids, w.S, n, K, d_g, ldS, st);
+  }
+  if (e == hipSuccess) e = launch_fill_f32(w.v, 0.f, K, st);
+  const int nblk = sinkhorn_blocks(n, K);
+  for (int t = 0; t < sinkhorn_iters && e == hipSuccess; ++t)
+    e = launch_sinkhorn_iter(w.S, n, K, ldS, w.v, w.partials, nblk, st);
+  if (e == hipSuccess) e = launch_topk(w.S, w.v, n, K, ldS, top_k, groups, st);
+  if (e == hipSuccess && col_potential)
+    e = hipMemcpyAsync(col_potential, w.v, sizeof(float) * K, hipMemcpyDeviceToDevice, st);
+  return hip_status(e);
+}
+
+// ============================================================================ bucket
+size_t focus_bucket_workspace_size(int batch, int64_t n, int K, int top_k) {
+  (void)top_k;
+  if (batch < 1 || n < 0 || K < 1) return 0;
+  const int64_t nchunks = (n + kBucketChunk - 1) / kBucketChunk;
+  Carver c(nullptr);
+  c.take<int32_t>((size_t)batch * K * (nchunks > 0 ? nchunks : 1));
+  c.take<int32_t>((size_t)batch * K);
+  return c.used;
+}
+
+int focus_bucket(const int32_t* groups, int batch, int64_t n, int K, int top_k, int32_t* offsets,
+                 int32_t* idx, int32_t* slot, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (batch < 1 || n < 0) return FOCUS_ERR_ARG;
+  if (int st = check_groups(K, top_k, 8)) return st;
+  if (n * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (!offsets) return FOCUS_ERR_ARG;
+  if (n > 0 && (!groups || !idx || !slot)) return FOCUS_ERR_ARG;
+  if (!aligned4(groups) || !aligned4(offsets) || !aligned4(idx) || !aligned4(slot) ||
+      !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  const size_t need = focus_bucket_workspace_size(batch, n, K, top_k);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+  Carver c(workspace);
+  const int64_t nchunks = (n + kBucketChunk - 1) / kBucketChunk;
+  int32_t* counts = c.take<int32_t>((size_t)batch * K * (nchunks > 0 ? nchunks : 1));
+  int32_t* totals = c.take<int32_t>((size_t)batch * K);
+  hipStream_t st = (hipStream_t)stream;
+  if (n == 0) return hip_status(launch_fill_i32(offsets, 0, (int64_t)batch * (K + 1), st));
+  return hip_status(launch_bucket(groups, batch, n, K, top_k, offsets, idx, slot, counts, totals,
+                                  st));
+}
+
+// ============================================================================ attention
+size_t focus_attention_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K, int top_k) {
+  if (n < 0 || Hq < 1 || Hkv < 1 || d_head < 1 || K < 1 || top_k < 1) return 0;
+  return attn_carve(nullptr, n, Hq, Hkv, d_head, K, top_k, nullptr);
+}
+
+int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int Hq,
+                       int Hkv, int d_head, const int32_t* groups, const int32_t* offsets,
+                       const int32_t* idx, const int32_t* slot, int K, int top_k, int64_t window,
+                       float scale, uint16_t* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* stage_events,
+                       int num_events) {
+  if (n < 0 || window < 0) return FOCUS_ERR_ARG;
+  if (num_events < 0 || num_events > 10 || (num_events > 0 && !stage_events)) return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  if (n * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (n == 0) return FOCUS_OK;
+  if (!q || !k || !v || !groups || !offsets || !idx || !slot || !out || !lse)
+    return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(groups) ||
+      !aligned4(offsets) || !aligned4(idx) || !aligned4(slot) || !aligned16(out) ||
+      !aligned4(lse) || !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  AttnWs w;
+  const size_t need = attn_carve(workspace, n, Hq, Hkv, d_head, K, top_k, &w);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+
+  AttnShape s{};
+  s.n = n;
+  s.nk = n * top_k;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
+  s.K = K;
+  s.top_k = top_k;
+  s.window = window < n + 1 ? window : n + 1;  // a window beyond the sequence is the whole past
+  s.scale = sc;
+  hipStream_t st = (hipStream_t)stream;
+  auto mark = [&](int i) -> hipError_t {
+    if (i >= num_events || !stage_events[i]) return hipSuccess;
+    return hipEventRecord((hipEvent_t)stage_events[i], st);
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_gather_qkv(q, k, v, idx, s, w.qg, w.kg, w.vg, st);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess) e = launch_tile_prefix(offsets, K, attn_tile_tokens(s.G), w.tile_pre, st);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess)
+    e = launch_group_attention(w.qg, w.kg, w.vg, offsets, w.tile_pre, idx, groups, s, w.og,
+                               w.lseg, st);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(6);
+  if (e == hipSuccess) e = launch_window_attention(q, k, v, s, w.ol, w.lsel, st);
+  if (e == hipSuccess) e = mark(7);
+  if (e == hipSuccess) e = mark(8);
+  if (e == hipSuccess) e = launch_merge(w.ol, w.lsel, w.og, w.lseg, slot, s, out, lse, st);
+  if (e == hipSuccess) e = mark(9);
+  return hip_status(e);
+}
+
+int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int Hq,
+                    int Hkv, int d_head, const int32_t* groups, const int32_t* offsets,
+                    const int32_t* idx, const int32_t* slot, int K, int top_k, int64_t window,
+                    float scale, uint16_t* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return focus_attention_ex(q, k, v, n, Hq, Hkv, d_head, groups, offsets, idx, slot, K, top_k,
+                            window, scale, out, lse, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+// ============================================================================ decode
+size_t focus_decode_workspace_size(int B, int64_t Lmax, int Hq, int Hkv, int d_head, int K,
+                                   int top_k) {
+  (void)Lmax;
+  (void)K;
+  (void)top_k;
+  if (B < 0 || Hq < 1 || Hkv < 1 || d_head < 1) return 0;
+  DecodeShape s{};
+  const int splits = decode_splits(s);
+  Carver c(nullptr);
+  c.take<float>((size_t)B * Hq * splits * d_head);
+  c.take<float>((size_t)B * Hq * splits * 2);
+  return c.used;
+}
+
+int focus_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_cache,
+                 const uint16_t* v_cache, const int32_t* cache_len, const int32_t* cache_groups,
+                 const int32_t* cache_offsets, const int32_t* cache_idx, int B, int64_t Lmax,
+                 int Hq, int Hkv, int d_head, int K, int top_k, int64_t window, float scale,
+                 uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (B < 0 || Lmax < 1 || window < 0) return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  if (Lmax * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (B == 0) return FOCUS_OK;
+  if (!q || !q_groups || !k_cache || !v_cache || !cache_len || !cache_groups || !cache_offsets ||
+      !cache_idx || !out || !lse)
+    return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned4(q_groups) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(cache_len) || !aligned4(cache_groups) || !aligned4(cache_offsets) ||
+      !aligned4(cache_idx) || !aligned16(out) || !aligned4(lse) || !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  const size_t need = focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+  DecodeShape s{};
+  s.B = B;
+  s.Lmax = Lmax;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
+  s.K = K;
+  s.top_k = top_k;
+  s.window = window;
+  s.scale = sc;
+  s.splits = decode_splits(s);
+  Carver c(workspace);
+  float* part_o = c.take<float>((size_t)B * Hq * s.splits * d_head);
+  float* part_ml = c.take<float>((size_t)B * Hq * s.splits * 2);
+  return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
+                                  cache_offsets, cache_idx, s, part_o, part_ml, out, lse,
+                                  (hipStream_t)stream));
+}
+
+}  // extern "C"

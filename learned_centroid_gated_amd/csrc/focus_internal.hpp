@@ -1,0 +1,113 @@
+// Internal declarations of the Focus HIP library (gfx950 / CDNA4): device helpers and the
+// host-side launchers each kernel source exports to the C-ABI layer in focus_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace focus {
+
+// ------------------------------------------------------------------ vector types
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, kWave); }
+__device__ __forceinline__ int shfl_xor_i(int x, int m) { return __shfl_xor(x, m, kWave); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+// Map a linear block id to a position in [0, total) so that each XCD receives one
+// contiguous range: block b is dispatched to XCD b % 8, so consecutive ranges of work
+// (and the data they share) stay in one XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
+  int64_t per = (total + kXcds - 1) / kXcds;
+  int64_t x = b % kXcds, j = b / kXcds;
+  if (j >= per) return -1;
+  int64_t c = x * per + j;
+  return c < total ? c : -1;
+}
+inline int64_t xcd_grid(int64_t total) {
+  int64_t per = (total + kXcds - 1) / kXcds;
+  return per * kXcds;
+}
+
+// ------------------------------------------------------------------ launchers
+// All launchers enqueue on `stream` and return hipSuccess or the launch error.
+
+// C[M, ldc] (first N columns) = A[M, Kd] * B[N, Kd]^T, fp32 in and out, fp32 MFMA.
+hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int64_t M, int N, int Kd,
+                              int ldc, hipStream_t stream);
+// Bt[N, Kd] = transpose of B[Kd, N], fp32.
+hipError_t launch_transpose_f32(const float* B, float* Bt, int Kd, int N, hipStream_t stream);
+// One Sinkhorn iteration on S [n, ldS] (first K columns): row step with the current v,
+// column partials per block, then the column step that overwrites v.
+hipError_t launch_sinkhorn_iter(const float* S, int64_t n, int K, int ldS, float* v, float2* partials,
+                                int nblocks, hipStream_t stream);
+int sinkhorn_blocks(int64_t n, int K);
+hipError_t launch_topk(const float* S, const float* v, int64_t n, int K, int ldS, int top_k,
+                       int32_t* groups, hipStream_t stream);
+hipError_t launch_fill_f32(float* p, float value, int64_t count, hipStream_t stream);
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t count, hipStream_t stream);
+
+// Stable counting sort of memberships (bucket).
+constexpr int kBucketChunk = 256;
+hipError_t launch_bucket(const int32_t* groups, int batch, int64_t n, int K, int top_k,
+                         int32_t* offsets, int32_t* idx, int32_t* slot, int32_t* counts,
+                         int32_t* totals, hipStream_t stream);
+
+// Attention pieces.
+struct AttnShape {
+  int64_t n;     // tokens
+  int64_t nk;    // memberships (n * top_k)
+  int Hq, Hkv, G, dh, K, top_k;
+  int64_t window;
+  float scale;   // natural-units logit scale
+};
+hipError_t launch_gather_qkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* idx, const AttnShape& s, uint16_t* qg, uint16_t* kg,
+                             uint16_t* vg, hipStream_t stream);
+hipError_t launch_tile_prefix(const int32_t* offsets, int K, int T, int32_t* tile_pre,
+                              hipStream_t stream);
+hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const uint16_t* vg,
+                                  const int32_t* offsets, const int32_t* tile_pre,
+                                  const int32_t* idx, const int32_t* groups, const AttnShape& s,
+                                  float* og, float* lseg, hipStream_t stream);
+hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const AttnShape& s, float* ol, float* lsel, hipStream_t stream);
+hipError_t launch_merge(const float* ol, const float* lsel, const float* og, const float* lseg,
+                        const int32_t* slot, const AttnShape& s, uint16_t* out, float* lse,
+                        hipStream_t stream);
+int attn_tile_tokens(int G);  // query tokens per attention tile: 128 / G
+
+// Decode.
+struct DecodeShape {
+  int B;
+  int64_t Lmax;
+  int Hq, Hkv, G, dh, K, top_k;
+  int64_t window;
+  float scale;
+  int splits;  // key-range splits per (sequence, kv head)
+};
+int decode_splits(const DecodeShape& s);
+hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
+                         const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
+                         const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
+                         float* part_o, float* part_ml, uint16_t* out, float* lse,
+                         hipStream_t stream);
+
+}  // namespace focus

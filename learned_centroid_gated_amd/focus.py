@@ -1,0 +1,152 @@
+"""Python binding of the Focus C ABI with the same entry-point names.
+
+Argument marshalling only: every step runs in libfocus.so's HIP kernels. torch provides device
+memory (outputs and workspace come from its caching allocator) and the current stream.
+"""
+import torch
+
+from . import _lib
+
+_lib_call = _lib.call
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (the Focus library has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ focus_assign
+def focus_assign_workspace_size(n, d, d_g, K):
+    return _lib.lib().focus_assign_workspace_size(n, d, d_g, K)
+
+
+def focus_assign(hidden, w_g, centroids, top_k, sinkhorn_iters, groups=None, col_potential=None,
+                 workspace=None, stream=None):
+    """Group assignment: returns (groups [n, top_k] int32, col_potential [K] fp32)."""
+    dev = hidden.device
+    _need(hidden, "hidden", torch.float32)
+    _need(w_g, "w_g", torch.float32, dev)
+    _need(centroids, "centroids", torch.float32, dev)
+    n, d = hidden.shape
+    d_g = w_g.shape[1]
+    K = centroids.shape[0]
+    if w_g.shape[0] != d or centroids.shape[1] != d_g:
+        raise ValueError("shape mismatch between hidden, w_g and centroids")
+    if groups is None:
+        groups = torch.empty((n, top_k), dtype=torch.int32, device=dev)
+    if col_potential is None:
+        col_potential = torch.empty((K,), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_assign_workspace_size(n, d, d_g, K), dev, workspace)
+    _lib_call("focus_assign", _ptr(hidden), _ptr(w_g), _ptr(centroids), n, d, d_g, K, top_k,
+              sinkhorn_iters, _ptr(groups), _ptr(col_potential), _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(stream))
+    return groups, col_potential
+
+
+# ------------------------------------------------------------------ focus_bucket
+def focus_bucket_workspace_size(batch, n, K, top_k):
+    return _lib.lib().focus_bucket_workspace_size(batch, n, K, top_k)
+
+
+def focus_bucket(groups, K, offsets=None, idx=None, slot=None, workspace=None, stream=None):
+    """groups [n, top_k] or [batch, n, top_k] int32 -> (offsets, idx, slot) with a batch dim
+    matching the input."""
+    _need(groups, "groups", torch.int32)
+    dev = groups.device
+    batched = groups.dim() == 3
+    g3 = groups if batched else groups.unsqueeze(0)
+    batch, n, top_k = g3.shape
+    if offsets is None:
+        offsets = torch.empty((batch, K + 1), dtype=torch.int32, device=dev)
+    if idx is None:
+        idx = torch.empty((batch, n * top_k), dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty((batch, n, top_k), dtype=torch.int32, device=dev)
+    ws = _workspace(focus_bucket_workspace_size(batch, n, K, top_k), dev, workspace)
+    _lib_call("focus_bucket", _ptr(g3), batch, n, K, top_k, _ptr(offsets), _ptr(idx), _ptr(slot),
+              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if batched:
+        return offsets, idx, slot
+    return offsets[0], idx[0], slot[0]
+
+
+# ------------------------------------------------------------------ focus_attention
+def focus_attention_workspace_size(n, Hq, Hkv, d_head, K, top_k):
+    return _lib.lib().focus_attention_workspace_size(n, Hq, Hkv, d_head, K, top_k)
+
+
+def focus_attention(q, k, v, groups, offsets, idx, slot, K, window, scale=0.0, out=None, lse=None,
+                    workspace=None, stream=None):
+    """Gated sparse causal attention: returns (out [n, Hq, dh] bf16, lse [n, Hq] fp32)."""
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, dev)
+    for t, name in ((groups, "groups"), (offsets, "offsets"), (idx, "idx"), (slot, "slot")):
+        _need(t, name, torch.int32, dev)
+    n, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    top_k = groups.shape[-1]
+    if out is None:
+        out = torch.empty((n, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((n, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_attention_workspace_size(n, Hq, Hkv, dh, K, top_k), dev, workspace)
+    _lib_call("focus_attention", _ptr(q), _ptr(k), _ptr(v), n, Hq, Hkv, dh, _ptr(groups),
+              _ptr(offsets), _ptr(idx), _ptr(slot), K, top_k, int(window), float(scale), _ptr(out),
+              _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return out, lse
+
+
+# ------------------------------------------------------------------ focus_decode
+def focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k):
+    return _lib.lib().focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k)
+
+
+def focus_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups, cache_offsets, cache_idx,
+                 K, window, scale=0.0, out=None, lse=None, workspace=None, stream=None):
+    """One token per sequence against its cache: returns (out [B, Hq, dh] bf16, lse [B, Hq])."""
+    dev = q.device
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, torch.bfloat16, dev)
+    for t, name in ((q_groups, "q_groups"), (cache_len, "cache_len"),
+                    (cache_groups, "cache_groups"), (cache_offsets, "cache_offsets"),
+                    (cache_idx, "cache_idx")):
+        _need(t, name, torch.int32, dev)
+    B, Hq, dh = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    top_k = q_groups.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_decode_workspace_size(B, Lmax, Hq, Hkv, dh, K, top_k), dev, workspace)
+    _lib_call("focus_decode", _ptr(q), _ptr(q_groups), _ptr(k_cache), _ptr(v_cache),
+              _ptr(cache_len), _ptr(cache_groups), _ptr(cache_offsets), _ptr(cache_idx), B, Lmax,
+              Hq, Hkv, dh, K, top_k, int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(stream))
+    return out, lse

@@ -1,0 +1,161 @@
+"""The C ABI: the library loads, exports every entry point include/focus.h declares, and rejects
+every bad-argument class on the host, before any launch (so these run without a GPU).
+
+Fake device pointers below are never dereferenced: each call fails validation first.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "focus.h")
+OK, ARG, SHAPE, UNSUP, ALIGN, WS = 0, -1, -2, -3, -4, -5
+P = 4096          # an aligned fake pointer
+MIS = 4096 + 2    # misaligned for every buffer kind
+BIG = 1 << 40     # a workspace size large enough for any case here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from learned_centroid_gated_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfocus.so not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(focus_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.focus_version() >= 100
+    for code in (OK, ARG, SHAPE, UNSUP, ALIGN, WS, -6):
+        assert lib.focus_status_string(code).decode().startswith("FOCUS_")
+    assert b"UNKNOWN" in lib.focus_status_string(-99)
+
+
+def _assign(lib, hidden=P, w=P, c=P, n=128, d=64, dg=16, K=8, top_k=2, iters=3, groups=P, v=P,
+            ws=P, wsb=BIG):
+    return lib.focus_assign(hidden, w, c, n, d, dg, K, top_k, iters, groups, v, ws, wsb, None)
+
+
+def test_assign_validation(lib):
+    assert _assign(lib, n=-1) == ARG
+    assert _assign(lib, dg=0) == ARG
+    assert _assign(lib, dg=2048) == ARG
+    assert _assign(lib, iters=-1) == ARG
+    assert _assign(lib, K=0) == ARG
+    assert _assign(lib, K=2000) == ARG
+    assert _assign(lib, top_k=0) == ARG
+    assert _assign(lib, top_k=9, K=8) == ARG
+    assert _assign(lib, top_k=9, K=16) == UNSUP
+    assert _assign(lib, d=66) == UNSUP
+    assert _assign(lib, dg=18) == UNSUP
+    assert _assign(lib, n=1 << 30, top_k=2) == SHAPE
+    assert _assign(lib, hidden=None) == ARG
+    assert _assign(lib, groups=None) == ARG
+    assert _assign(lib, hidden=MIS) == ALIGN
+    assert _assign(lib, v=MIS) == ALIGN
+    assert _assign(lib, ws=MIS) == ALIGN
+    assert _assign(lib, ws=None) == WS
+    assert _assign(lib, wsb=16) == WS
+    assert _assign(lib, n=0, hidden=None, groups=None) == OK  # empty: nothing enqueued
+
+
+def test_assign_workspace_size(lib):
+    f = lib.focus_assign_workspace_size
+    assert f(-1, 8, 8, 8) == 0
+    a, b = f(1000, 768, 64, 16), f(2000, 768, 64, 16)
+    assert 0 < a < b
+    # the scores alone take n * K floats
+    assert f(1 << 20, 4096, 128, 256) >= (1 << 20) * 256 * 4
+
+
+def _bucket(lib, groups=P, batch=1, n=100, K=8, top_k=2, off=P, idx=P, slot=P, ws=P, wsb=BIG):
+    return lib.focus_bucket(groups, batch, n, K, top_k, off, idx, slot, ws, wsb, None)
+
+
+def test_bucket_validation(lib):
+    assert _bucket(lib, batch=0) == ARG
+    assert _bucket(lib, n=-5) == ARG
+    assert _bucket(lib, K=0) == ARG
+    assert _bucket(lib, top_k=9, K=16) == UNSUP
+    assert _bucket(lib, top_k=3, K=2) == ARG
+    assert _bucket(lib, n=1 << 31, top_k=1) == SHAPE
+    assert _bucket(lib, off=None) == ARG
+    assert _bucket(lib, idx=None) == ARG
+    assert _bucket(lib, slot=MIS) == ALIGN
+    assert _bucket(lib, wsb=0) == WS
+    assert lib.focus_bucket_workspace_size(2, 1000, 16, 2) >= 2 * 16 * 4 * 4
+
+
+def _attn(lib, q=P, k=P, v=P, n=256, Hq=8, Hkv=2, dh=128, groups=P, off=P, idx=P, slot=P, K=8,
+          top_k=2, window=16, scale=0.0, out=P, lse=P, ws=P, wsb=BIG):
+    return lib.focus_attention(q, k, v, n, Hq, Hkv, dh, groups, off, idx, slot, K, top_k, window,
+                               scale, out, lse, ws, wsb, None)
+
+
+def test_attention_validation(lib):
+    assert _attn(lib, n=-1) == ARG
+    assert _attn(lib, window=-1) == ARG
+    assert _attn(lib, Hq=6, Hkv=4) == ARG
+    assert _attn(lib, Hq=6, Hkv=2) == UNSUP   # G = 3
+    assert _attn(lib, Hq=64, Hkv=2) == UNSUP  # G = 32
+    assert _attn(lib, dh=96) == UNSUP
+    assert _attn(lib, top_k=5, K=8) == UNSUP
+    assert _attn(lib, top_k=9, K=8) == ARG
+    assert _attn(lib, scale=math.nan) == ARG
+    assert _attn(lib, scale=math.inf) == ARG
+    assert _attn(lib, n=1 << 30, top_k=2) == SHAPE
+    assert _attn(lib, q=None) == ARG
+    assert _attn(lib, slot=None) == ARG
+    assert _attn(lib, lse=MIS) == ALIGN
+    assert _attn(lib, wsb=1) == WS
+    assert _attn(lib, n=0, q=None) == OK
+
+
+def test_attention_workspace_size(lib):
+    f = lib.focus_attention_workspace_size
+    n, Hq, Hkv, dh, K, k = 131072, 64, 8, 128, 128, 2
+    # gathered Q/K/V (bf16) plus fp32 partials of both passes
+    floor = n * k * (Hq + 2 * Hkv) * dh * 2 + n * k * Hq * dh * 4 + n * Hq * dh * 4
+    assert f(n, Hq, Hkv, dh, K, k) >= floor
+
+
+def _decode(lib, q=P, qg=P, kc=P, vc=P, ln=P, cg=P, co=P, ci=P, B=4, L=1024, Hq=8, Hkv=2, dh=128,
+            K=16, top_k=2, window=64, scale=0.0, out=P, lse=P, ws=P, wsb=BIG):
+    return lib.focus_decode(q, qg, kc, vc, ln, cg, co, ci, B, L, Hq, Hkv, dh, K, top_k, window,
+                            scale, out, lse, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, B=-1) == ARG
+    assert _decode(lib, L=0) == ARG
+    assert _decode(lib, window=-3) == ARG
+    assert _decode(lib, dh=32) == UNSUP
+    assert _decode(lib, top_k=5) == UNSUP
+    assert _decode(lib, L=1 << 31, top_k=1) == SHAPE
+    assert _decode(lib, cg=None) == ARG
+    assert _decode(lib, ci=MIS) == ALIGN
+    assert _decode(lib, wsb=0) == WS
+    assert _decode(lib, B=0, q=None) == OK
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    from learned_centroid_gated_amd import focus_assign
+    with pytest.raises(ValueError, match="device tensor"):
+        focus_assign(torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(2, 4), 1, 1)
