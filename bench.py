@@ -1,0 +1,394 @@
+#!/usr/bin/env python
+"""Focus inference-path benchmark on one MI355X.
+
+A step is one pass of the prefill hot path over one synthetic sequence with every input already
+resident in HBM: focus_assign (scores, Sinkhorn, top-k) -> focus_bucket -> focus_attention
+(gather, group pass, window pass, merge). The headline line is the 128K-token 70B-shaped GQA
+layer; the 1M-token prefill, the batched decode and a dense causal baseline on the same GPU are
+reported beside it. Kernel times inside focus_attention come from HIP events the library records
+on its own stream around each stage (focus_attention_ex).
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--quick]
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_size,  # noqa: E402
+                                        focus_attention, focus_attention_workspace_size,
+                                        focus_bucket, focus_bucket_workspace_size, focus_decode)
+from learned_centroid_gated_amd import _lib  # noqa: E402
+from synth import CONFIGS, assign_inputs, qkv_inputs, random_groups  # noqa: E402
+
+METRIC = "Focus prefill tokens/s/GPU at 128K & 1M; attn TFLOP/s as % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+STAGES = ("gather", "tile_prefix", "group_attention", "window_attention", "merge")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ HIP events (ctypes)
+class Hip:
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def attention_ex(hip, q, k, v, groups, off, idx, slot, K, window, out, lse, ws, events):
+    n, Hq, dh = q.shape
+    arr = (ctypes.c_void_p * 10)(*events)
+    _lib.call("focus_attention_ex", q.data_ptr(), k.data_ptr(), v.data_ptr(), n, Hq, k.shape[1], dh,
+              groups.data_ptr(), off.data_ptr(), idx.data_ptr(), slot.data_ptr(), K,
+              groups.shape[1], int(window), 0.0, out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+              ws.numel(), torch.cuda.current_stream().cuda_stream, arr, 10)
+
+
+# ------------------------------------------------------------------ prefill
+def window_pairs(n, w):
+    i = np.arange(n, dtype=np.int64)
+    return int(np.minimum(i + 1, w).sum())
+
+
+def count_allowed_pairs(k, v, groups, off, idx, slot, K, window):
+    """Exact allowed-pair count from the product path's Q = 0 run: every logit is 0, so
+    exp(lse_i) is the number of keys row i attends (the tests pin this against the oracle)."""
+    n = k.shape[0]
+    q0 = torch.zeros((n, 1, k.shape[2]), dtype=torch.bfloat16, device="cuda")
+    k1, v1 = k[:, :1].contiguous(), v[:, :1].contiguous()
+    _, lse = focus_attention(q0, k1, v1, groups, off, idx, slot, K, window)
+    counts = torch.exp(lse[:, 0].double()).round().to(torch.int64)
+    return int(counts.sum().item())
+
+
+def prefill_bench(c, steps, warmup, hip):
+    log(f"[bench] prefill {c.name}: n={c.n} d={c.d} Hq={c.Hq}/{c.Hkv} dh={c.dh} K={c.K} "
+        f"top_k={c.top_k} window={c.window} iters={c.iters}")
+    t0 = time.time()
+    a = assign_inputs(c.n, c.d, c.dg, c.K, c.mix, c.weights, c.noise_frac, index=c.index,
+                      device="cuda")
+    t = qkv_inputs(c.n, c.Hq, c.Hkv, c.dh, index=c.index, device="cuda")
+    hidden, w_g, cents = a["hidden"], a["w_g"], a["centroids"]
+    q, k, v = t["q"], t["k"], t["v"]
+    dev = q.device
+    groups = torch.empty((c.n, c.top_k), dtype=torch.int32, device=dev)
+    vpot = torch.empty((c.K,), dtype=torch.float32, device=dev)
+    off = torch.empty((c.K + 1,), dtype=torch.int32, device=dev)
+    idx = torch.empty((c.n * c.top_k,), dtype=torch.int32, device=dev)
+    slot = torch.empty((c.n, c.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((c.n, c.Hq, c.dh), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((c.n, c.Hq), dtype=torch.float32, device=dev)
+    ws_a = torch.empty(focus_assign_workspace_size(c.n, c.d, c.dg, c.K), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(focus_bucket_workspace_size(1, c.n, c.K, c.top_k), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(focus_attention_workspace_size(c.n, c.Hq, c.Hkv, c.dh, c.K, c.top_k),
+                       dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench]   inputs resident in {time.time() - t0:.1f}s; workspaces "
+        f"{(ws_a.numel() + ws_b.numel() + ws_t.numel()) / 2**30:.1f} GiB")
+
+    stage_ev = [[hip.event() for _ in range(10)] for _ in range(steps)]
+    call_ev = [[hip.event() for _ in range(3)] for _ in range(steps)]
+    rec = hip.h.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i=None):
+        if i is not None:
+            rec(call_ev[i][0], stream)
+        focus_assign(hidden, w_g, cents, c.top_k, c.iters, groups=groups, col_potential=vpot,
+                     workspace=ws_a)
+        if i is not None:
+            rec(call_ev[i][1], stream)
+        focus_bucket(groups, c.K, off[None], idx[None], slot[None], workspace=ws_b)
+        if i is not None:
+            rec(call_ev[i][2], stream)
+        attention_ex(hip, q, k, v, groups, off, idx, slot, c.K, c.window, out, lse, ws_t,
+                     stage_ev[i] if i is not None else [None] * 10)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.time()
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / steps
+    assign_ms = np.mean([hip.elapsed_ms(e[0], e[1]) for e in call_ev])
+    bucket_ms = np.mean([hip.elapsed_ms(e[1], e[2]) for e in call_ev])
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * s], e[2 * s + 1]) for e in stage_ev]))
+                for s, name in enumerate(STAGES)}
+    for e in stage_ev + call_ev:
+        for x in e:
+            hip.destroy(x)
+
+    # effective FLOPs on the exact allowed-pair count (untimed accounting pass)
+    pairs = count_allowed_pairs(k, v, groups, off, idx, slot, c.K, c.window)
+    wpairs = window_pairs(c.n, c.window)
+    gpairs = pairs - wpairs
+    flops_pair = 4.0 * c.dh * c.Hq
+    sizes = torch.bincount(groups.flatten().long(), minlength=c.K).cpu().numpy()
+    nk = c.n * c.top_k
+    res = {
+        "workload": c.name, "n": c.n, "ms_per_step": ms, "wall_s": wall, "steps": steps,
+        "tokens_per_s": c.n / (ms / 1e3),
+        "assign_ms": float(assign_ms), "bucket_ms": float(bucket_ms),
+        "attention_stage_ms": stage_ms,
+        "allowed_pairs": pairs, "window_pairs": wpairs, "group_pairs": gpairs,
+        "density_vs_causal": pairs / (c.n * (c.n + 1) / 2),
+        "segment_sizes": {"min": int(sizes.min()), "mean": float(sizes.mean()), "max": int(sizes.max())},
+    }
+    attn_ms = stage_ms["group_attention"] + stage_ms["window_attention"]
+    res["attention_tflops"] = flops_pair * pairs / (attn_ms * 1e-3) / 1e12
+    res["attention_pct_bf16_peak"] = 100 * res["attention_tflops"] / PEAK_BF16_TFLOPS
+    res["group_tflops"] = flops_pair * gpairs / (stage_ms["group_attention"] * 1e-3) / 1e12
+    res["window_tflops"] = flops_pair * wpairs / (stage_ms["window_attention"] * 1e-3) / 1e12
+    # algorithmic bytes of the HBM-bound stages
+    bpe = 2  # bf16
+    gather_bytes = nk * (c.Hq + 2 * c.Hkv) * c.dh * bpe * 2          # read + write per membership
+    merge_bytes = c.n * c.Hq * (c.dh * 4 + 4) * (1 + c.top_k) + c.n * c.Hq * (c.dh * bpe + 4)
+    res["gather_GBs"] = gather_bytes / (stage_ms["gather"] * 1e-3) / 1e9
+    res["merge_GBs"] = merge_bytes / (stage_ms["merge"] * 1e-3) / 1e9
+    assign_flops = 2.0 * c.n * c.d * (c.K if c.d * c.K <= c.d * c.dg + c.dg * c.K else c.dg) + \
+        (0 if c.d * c.K <= c.d * c.dg + c.dg * c.K else 2.0 * c.n * c.dg * c.K)
+    res["assign_fp32_tflops"] = assign_flops / (assign_ms * 1e-3) / 1e12
+    res["assign_hidden_GBs"] = c.n * c.d * 4 / (assign_ms * 1e-3) / 1e9
+    # the dominant kernel of the step
+    dom = max(("group_attention", "window_attention", "gather", "merge"), key=lambda s: stage_ms[s])
+    if dom in ("group_attention", "window_attention"):
+        p = gpairs if dom == "group_attention" else wpairs
+        ach = flops_pair * p / (stage_ms[dom] * 1e-3) / 1e12
+        res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "algorithmic_per_launch": flops_pair * p}
+    else:
+        b = gather_bytes if dom == "gather" else merge_bytes
+        ach = b / (stage_ms[dom] * 1e-3) / 1e9
+        res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                           "algorithmic_per_launch": b}
+    log(f"[bench]   {ms:.3f} ms/step  {res['tokens_per_s']:.4g} tok/s  stages {stage_ms} "
+        f"assign {assign_ms:.3f} bucket {bucket_ms:.3f}")
+    state = dict(q=q, k=k, v=v, groups=groups, off=off, idx=idx, slot=slot, out=out, lse=lse,
+                 ws_t=ws_t)
+    del hidden, w_g, cents, a, t, ws_a, ws_b
+    return res, state
+
+
+def dense_baseline(c, st, hip, reps=2):
+    """Dense causal attention on the same GPU: our window kernel with window = n, and torch's
+    scaled_dot_product_attention(is_causal=True) on the same Q/K/V."""
+    q, k, v = st["q"], st["k"], st["v"]
+    out, lse, ws = st["out"], st["lse"], st["ws_t"]
+    ev = [hip.event() for _ in range(10)]
+    times = []
+    for r in range(reps + 1):
+        attention_ex(hip, q, k, v, st["groups"], st["off"], st["idx"], st["slot"], c.K, c.n, out,
+                     lse, ws, ev)
+        torch.cuda.synchronize()
+        if r:
+            times.append(hip.elapsed_ms(ev[6], ev[7]))
+    for e in ev:
+        hip.destroy(e)
+    own_ms = float(np.mean(times))
+    causal_flops = 4.0 * c.dh * c.Hq * c.n * (c.n + 1) / 2
+    res = {"own_window_kernel_ms": own_ms,
+           "own_window_kernel_tflops": causal_flops / (own_ms * 1e-3) / 1e12}
+    try:
+        G = c.Hq // c.Hkv
+        qt = q.permute(1, 0, 2).unsqueeze(0)
+        kt = k.repeat_interleave(G, dim=1).permute(1, 0, 2).unsqueeze(0)
+        vt = v.repeat_interleave(G, dim=1).permute(1, 0, 2).unsqueeze(0)
+        times = []
+        for r in range(reps + 1):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+            e.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(s.elapsed_time(e))
+        res["torch_sdpa_causal_ms"] = float(np.mean(times))
+        res["torch_sdpa_causal_tflops"] = causal_flops / (res["torch_sdpa_causal_ms"] * 1e-3) / 1e12
+        del qt, kt, vt
+    except Exception as ex:  # report, do not fail the bench
+        res["torch_sdpa_causal_error"] = f"{type(ex).__name__}: {str(ex)[:160]}"
+    return res
+
+
+# ------------------------------------------------------------------ decode
+def decode_bench(c, steps, warmup):
+    log(f"[bench] decode {c.name}: B={c.batch} L={c.n} Hq={c.Hq}/{c.Hkv} K={c.K} top_k={c.top_k} "
+        f"window={c.window}")
+    B, L = c.batch, c.n
+    dev = torch.device("cuda:0")
+    cache_groups = torch.empty((B, L, c.top_k), dtype=torch.int32, device=dev)
+    for b in range(B):  # cached memberships: assignment of each sequence's mixture hidden states
+        a = assign_inputs(L, c.d, c.dg, c.K, c.mix, c.weights, index=c.index, salt=b + 1, device="cuda")
+        focus_assign(a["hidden"], a["w_g"], a["centroids"], c.top_k, c.iters, groups=cache_groups[b])
+        del a
+    fresh = assign_inputs(B, c.d, c.dg, c.K, c.mix, c.weights, index=c.index, salt=100, device="cuda")
+    q_groups, _ = focus_assign(fresh["hidden"], fresh["w_g"], fresh["centroids"], c.top_k, c.iters)
+    t = qkv_inputs(L, c.Hq, c.Hkv, c.dh, index=c.index, device="cuda", lead=(B,), which="kv")
+    qd = qkv_inputs(1, c.Hq, c.Hkv, c.dh, index=c.index, salt=1, device="cuda", lead=(B,),
+                    which="q")["q"][:, 0].contiguous()
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    off, idx, _ = focus_bucket(cache_groups, c.K)
+    out = torch.empty((B, c.Hq, c.dh), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, c.Hq), dtype=torch.float32, device=dev)
+
+    def step():
+        focus_decode(qd, q_groups, t["k"], t["v"], lens, cache_groups, off, idx, c.K, c.window,
+                     out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / steps
+    # keys per query from a Q = 0 decode: exp(lse) counts the allowed keys
+    focus_decode(torch.zeros_like(qd), q_groups, t["k"], t["v"], lens, cache_groups, off, idx, c.K,
+                 c.window, out=out, lse=lse)
+    keys = torch.exp(lse[:, 0].double()).round().sum().item()
+    kv_bytes = keys * c.Hkv * c.dh * 2 * 2
+    res = {"workload": c.name, "us_per_step": us, "allowed_keys_per_query": keys / B,
+           "kv_GBs": kv_bytes / (us * 1e-6) / 1e9}
+    res["kv_pct_hbm_peak"] = 100 * res["kv_GBs"] / PEAK_HBM_GBS
+    log(f"[bench]   decode {us:.1f} us/step, {keys / B:.0f} keys/query, {res['kv_GBs']:.0f} GB/s")
+    return res
+
+
+# ------------------------------------------------------------------ oracle on the host
+def cpu_baseline(c, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample of the same workload: assignment of a block of
+    tokens with the workload's shapes, plus attention rows drawn uniformly from the full
+    sequence; tokens/s = 1 / (assign seconds per token + attention seconds per row)."""
+    from oracle import assign_ref, attention_rows_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    n_a = min(c.n, 4096)
+    a = assign_inputs(n_a, c.d, c.dg, c.K, c.mix, c.weights, c.noise_frac, index=c.index, salt=7)
+    t0 = time.time()
+    assign_ref(a["hidden"], a["w_g"], a["centroids"], c.top_k, c.iters)
+    t_assign = (time.time() - t0) / n_a
+    del a
+    kv = qkv_inputs(c.n, c.Hq, c.Hkv, c.dh, index=c.index, salt=8, which="kv")
+    groups = random_groups(c.n, c.K, c.top_k, np.random.default_rng(c.index))
+    rng = np.random.default_rng(1)
+    rows, t_rows = [], 0.0
+    while t_rows < budget_s and len(rows) < 256:
+        i = int(rng.integers(c.n))
+        # the oracle reads q only at row i: a stride-0 view stands in for the full array
+        q_row = qkv_inputs(1, c.Hq, 1, c.dh, index=c.index, salt=10 + len(rows), which="q")["q"]
+        qi = np.broadcast_to(q_row, (c.n, c.Hq, c.dh))
+        t0 = time.time()
+        attention_rows_ref(qi, kv["k"], kv["v"], groups, c.window, rows=[i])
+        t_rows += time.time() - t0
+        rows.append(i)
+    t_attn = t_rows / len(rows)
+    tok_s = 1.0 / (t_assign + t_attn)
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "blas_threads": threads,
+            "kind": "oracle",
+            "sample": f"assign_ref on {n_a} tokens of the {c.name} shapes ({t_assign * n_a:.1f}s) "
+                      f"+ attention_rows_ref on {len(rows)} uniformly drawn rows of the full "
+                      f"{c.n}-token sequence ({t_rows:.1f}s); tokens/s = 1/(s/token + s/row)"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the Focus path here runs on a single MI355X and has no "
+              "multi-GPU mode (see the sharding design in DESIGN.md); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+    cfg = {x.name: x for x in CONFIGS}
+    c3 = cfg["gqa70b_n128k"]
+    res3, st3 = prefill_bench(c3, args.steps, args.warmup, hip)
+    extra = {}
+    if not args.quick:
+        extra["dense_baseline_128k"] = dense_baseline(c3, st3, hip)
+        extra["dense_baseline_128k"]["focus_speedup_vs_own_dense"] = (
+            extra["dense_baseline_128k"]["own_window_kernel_ms"] / res3["ms_per_step"])
+    del st3
+    torch.cuda.empty_cache()
+    if not args.quick:
+        res4, st4 = prefill_bench(cfg["long_n1m"], max(3, args.steps // 2), 1, hip)
+        extra["long_n1m"] = res4
+        del st4
+        torch.cuda.empty_cache()
+        extra["decode_b64_l64k"] = decode_bench(cfg["decode_b64_l64k"], 20, 3)
+        torch.cuda.empty_cache()
+    line = {
+        "metric": METRIC, "value": res3["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res3["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian-mixture fp32 hidden states, N(0,1) bf16 Q/K/V",
+        "config": {"workload": c3.name, "n": c3.n, "d_model": c3.d, "q_heads": c3.Hq,
+                   "kv_heads": c3.Hkv, "d_head": c3.dh, "d_g": c3.dg, "K": c3.K,
+                   "top_k": c3.top_k, "window": c3.window, "sinkhorn_iters": c3.iters,
+                   "global_batch": 1, "seq_len": c3.n, "parallelism": "single GPU"},
+        "roofline": res3.pop("roofline"),
+        "attention_tflops": res3["attention_tflops"],
+        "attention_pct_bf16_peak": res3["attention_pct_bf16_peak"],
+        "detail_128k": res3,
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(c3)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,15 +23,20 @@ namespace focus {
 int attn_tile_tokens(int G) { return 128 / G; }
 
 // ============================================================================ gather
-// qg[s] = q[idx[s]], kg[s] = k[idx[s]], vg[s] = v[idx[s]] for every membership slot s.
+// qg[s] = q[idx[s]], kg[s] = k[idx[s]], vg[s] = v[idx[s]] for every membership slot s, and
+// kinfo[s] = (token position, the token's groups below this segment's group, -1 padded): the
+// pair rule of the group pass needs only these, so its inner loop makes no dependent loads.
 __global__ __launch_bounds__(256) void gather_qkv_kernel(const i32x4_t* __restrict__ q,
                                                          const i32x4_t* __restrict__ k,
                                                          const i32x4_t* __restrict__ v,
                                                          const int32_t* __restrict__ idx,
-                                                         int64_t nk, int cq, int ckv,
+                                                         const int32_t* __restrict__ groups,
+                                                         const int32_t* __restrict__ slot,
+                                                         int top_k, int64_t nk, int cq, int ckv,
                                                          i32x4_t* __restrict__ qg,
                                                          i32x4_t* __restrict__ kg,
-                                                         i32x4_t* __restrict__ vg) {
+                                                         i32x4_t* __restrict__ vg,
+                                                         i32x4_t* __restrict__ kinfo) {
   const int per = cq + 2 * ckv;  // 16-byte chunks per slot
   const int64_t total = nk * per;
   const int64_t stride = (int64_t)gridDim.x * 256 * 4;
@@ -48,6 +53,17 @@ __global__ __launch_bounds__(256) void gather_qkv_kernel(const i32x4_t* __restri
       int c = (int)(e - s * per);
       int32_t tok = idx[s];
       if (tok < 0) continue;
+      if (c == 0) {
+        // the membership's rank r among the token's (ascending) groups: lower groups come first
+        i32x4_t info = {tok, -1, -1, -1};
+        for (int r = 0; r < top_k; ++r) {
+          if (slot[(int64_t)tok * top_k + r] == (int32_t)s) {
+            for (int c2 = 0; c2 < r && c2 < 3; ++c2) info[1 + c2] = groups[(int64_t)tok * top_k + c2];
+            break;
+          }
+        }
+        kinfo[s] = info;
+      }
       if (c < cq) {
         val[u] = q[(int64_t)tok * cq + c];
         dst[u] = s * cq + c;
@@ -74,16 +90,17 @@ __global__ __launch_bounds__(256) void gather_qkv_kernel(const i32x4_t* __restri
 }
 
 hipError_t launch_gather_qkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             const int32_t* idx, const AttnShape& s, uint16_t* qg, uint16_t* kg,
-                             uint16_t* vg, hipStream_t stream) {
+                             const int32_t* idx, const int32_t* groups, const int32_t* slot,
+                             const AttnShape& s, uint16_t* qg, uint16_t* kg, uint16_t* vg,
+                             int32_t* kinfo, hipStream_t stream) {
   const int cq = s.Hq * s.dh / 8, ckv = s.Hkv * s.dh / 8;
   int64_t total = s.nk * (cq + 2 * ckv);
   int64_t blocks = (total + 1023) / 1024;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(gather_qkv_kernel, dim3(blocks), dim3(256), 0, stream, (const i32x4_t*)q,
-                     (const i32x4_t*)k, (const i32x4_t*)v, idx, s.nk, cq, ckv, (i32x4_t*)qg,
-                     (i32x4_t*)kg, (i32x4_t*)vg);
+                     (const i32x4_t*)k, (const i32x4_t*)v, idx, groups, slot, s.top_k, s.nk, cq,
+                     ckv, (i32x4_t*)qg, (i32x4_t*)kg, (i32x4_t*)vg, (i32x4_t*)kinfo);
   return hipGetLastError();
 }
 
@@ -130,27 +147,29 @@ struct FlashArgs {
   float sl2;          // scale * log2(e)
   const int32_t* seg_off;   // group: [K+1]
   const int32_t* tile_pre;  // group: [K+1]
-  const int32_t* pos;       // group: slot -> token position
-  const int32_t* groups;    // group: [n, top_k], ascending
-  int K, top_k;
+  const i32x4_t* kinfo;     // group: per slot (position, lower groups, -1 padded)
+  int K;
   int tiles_per_head;       // window: ceil(n / T)
 };
 
 constexpr int KT = 64;  // keys per kv tile
-constexpr int kMaxLow = 3;
 
 template <int DH>
 struct FlashSmem {
-  static constexpr int KS = DH + 8;      // K tile row stride (bf16 elements)
-  static constexpr int VS = KT + 8;      // transposed V row stride (bf16 elements)
+  static constexpr int KS = DH + 8;  // K tile row stride (bf16): 16 rows cover all banks
+  static constexpr int VS = KT + 4;  // transposed V row stride (bf16): 32 rows, distinct banks
   __bf16 k[KT * KS];
   __bf16 vt[DH * VS];
   int kpos[KT];
-  int klow[KT * kMaxLow];
+  int klow[3][KT];
 };
 
-template <int DH, bool GROUP>
-__global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
+// Tile classes seen by one wave.
+enum { kSkip = 0, kEdge = 1, kFar = 2, kFull = 3 };
+
+// NLOW = top_k - 1 lower groups per membership matter for the ownership rule (group pass).
+template <int DH, bool GROUP, int NLOW>
+__global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   using Smem = FlashSmem<DH>;
   constexpr int KS = Smem::KS, VS = Smem::VS;
   constexpr int CH = DH / 8;        // 16-byte chunks per row
@@ -170,24 +189,19 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
   const int h = (int)(comb / W);
   const int item = (int)(comb - (int64_t)h * W);
 
-  int64_t q0, q1;        // query index range [q0, q1): slots (group) or tokens (window)
-  int64_t kv_lo;         // first key index
-  int grp = 0;
-  int64_t seg_hi = 0;
+  int64_t q0, q1, kv_lo;
   if constexpr (GROUP) {
-    int lo = 0, hi = a.K - 1;  // largest g with tile_pre[g] <= item
+    int lo = 0, hi = a.K - 1;  // largest g with tile_pre[g] <= item (a non-empty segment)
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
       if (a.tile_pre[mid] <= item) lo = mid;
       else hi = mid - 1;
     }
-    grp = lo;
-    const int nt = a.tile_pre[grp + 1] - a.tile_pre[grp];
-    const int t = nt - 1 - (item - a.tile_pre[grp]);  // heaviest tiles first
-    const int64_t s_lo = a.seg_off[grp];
-    seg_hi = a.seg_off[grp + 1];
+    const int nt = a.tile_pre[lo + 1] - a.tile_pre[lo];
+    const int t = nt - 1 - (item - a.tile_pre[lo]);  // heaviest tiles of a segment first
+    const int64_t s_lo = a.seg_off[lo], s_hi = a.seg_off[lo + 1];
     q0 = s_lo + (int64_t)t * a.T;
-    q1 = q0 + a.T < seg_hi ? q0 + a.T : seg_hi;
+    q1 = q0 + a.T < s_hi ? q0 + a.T : s_hi;
     kv_lo = s_lo;
   } else {
     q0 = (int64_t)item * a.T;
@@ -202,35 +216,28 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
   const int hq = h * a.G + head_local;
   const int64_t qi = q0 + tok_local;
   const bool qvalid = qi < q1;
-  // token range of the wave's rows (rows of one wave are consecutive tokens of one head,
-  // or all T tokens of the tile when T < 32)
   const int wt0 = (wave * 32) % a.T;
   const int wtn = a.T < 32 ? a.T : 32;
   const int64_t wq_lo = q0 + wt0;
   const int64_t wq_hi = (q0 + wt0 + wtn < q1 ? q0 + wt0 + wtn : q1) - 1;
   const bool wave_active = wq_hi >= wq_lo;
 
-  int qpos = 0;
-  int qlow[kMaxLow] = {-1, -1, -1};
+  int qpos = 0, wpos_lo = 0, wpos_hi = 0, tpos_hi = 0;
+  int qlow[3] = {-2, -2, -2};
   if constexpr (GROUP) {
     if (qvalid) {
-      qpos = a.pos[qi];
-      int c = 0;
-      for (int rr = 0; rr < a.top_k; ++rr) {
-        int gg = a.groups[(int64_t)qpos * a.top_k + rr];
-        if (gg < grp && c < kMaxLow) qlow[c++] = gg;
-      }
+      i32x4_t qinfo = a.kinfo[qi];
+      qpos = qinfo[0];
+#pragma unroll
+      for (int c = 0; c < NLOW; ++c) qlow[c] = qinfo[1 + c] >= 0 ? qinfo[1 + c] : -2;
     }
+    if (wave_active) {
+      wpos_lo = a.kinfo[wq_lo][0];
+      wpos_hi = a.kinfo[wq_hi][0];
+    }
+    tpos_hi = a.kinfo[kv_hi][0];
   } else {
     qpos = (int)qi;
-  }
-  int wpos_lo = 0, wpos_hi = 0, tpos_hi = 0;
-  if constexpr (GROUP) {
-    if (wave_active) {
-      wpos_lo = a.pos[wq_lo];
-      wpos_hi = a.pos[wq_hi];
-    }
-    tpos_hi = a.pos[kv_hi];
   }
 
   bf16x8_t qreg[NS];
@@ -242,14 +249,13 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
   }
 
   // ---------------------------------------------------------------- kv tile range
-  int64_t ntiles = 0;
+  int64_t ntiles;
   if constexpr (GROUP) {
-    // stop at the first tile whose pairs all fall inside the window (positions ascend)
-    int64_t hi_t = (kv_hi - kv_lo) / KT + 1;
-    int64_t lo_t = 0;
-    while (lo_t < hi_t) {  // first tile t with tpos_hi - pos[kv_lo + t*KT] < window
+    // tiles up to the first one whose pairs all fall inside the window (positions ascend)
+    int64_t lo_t = 0, hi_t = (kv_hi - kv_lo) / KT + 1;
+    while (lo_t < hi_t) {
       int64_t mid = (lo_t + hi_t) >> 1;
-      if ((int64_t)tpos_hi - a.pos[kv_lo + mid * KT] < a.window) hi_t = mid;
+      if ((int64_t)tpos_hi - a.kinfo[kv_lo + mid * KT][0] < a.window) hi_t = mid;
       else lo_t = mid + 1;
     }
     ntiles = lo_t;
@@ -262,41 +268,29 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
   for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // register staging of the next tile
   bf16x8_t kreg[KPASS];
   bf16x8_t vreg[VKPT];
-  int kpos_reg = 0;
-  int klow_reg[kMaxLow] = {-2, -2, -2};
+  i32x4_t ireg = {0x7fffffff, -1, -1, -1};
   const int lc = tid % CH, lr = tid / CH;
+  const int64_t kstride = (int64_t)a.Hkv * DH;
+  const uint16_t* kbase = a.k + (int64_t)h * DH + lc * 8;
+  const uint16_t* vbase = a.v + (int64_t)h * DH + lc * 8;
 
   auto load_tile = [&](int64_t ks) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
       int64_t row = ks + lr + p * RPP;
-      kreg[p] = row <= kv_hi
-                    ? *(const bf16x8_t*)(a.k + (row * a.Hkv + h) * (int64_t)DH + lc * 8)
-                    : bf16x8_t{};
+      kreg[p] = row <= kv_hi ? *(const bf16x8_t*)(kbase + row * kstride) : bf16x8_t{};
     }
 #pragma unroll
     for (int e = 0; e < VKPT; ++e) {
       int64_t row = ks + lr * VKPT + e;
-      vreg[e] = row <= kv_hi
-                    ? *(const bf16x8_t*)(a.v + (row * a.Hkv + h) * (int64_t)DH + lc * 8)
-                    : bf16x8_t{};
+      vreg[e] = row <= kv_hi ? *(const bf16x8_t*)(vbase + row * kstride) : bf16x8_t{};
     }
     if constexpr (GROUP) {
       if (tid < KT) {
         int64_t row = ks + tid;
-        kpos_reg = row <= kv_hi ? a.pos[row] : 0x7fffffff;
-        if (a.top_k > 1) {
-          int c = 0;
-          klow_reg[0] = klow_reg[1] = klow_reg[2] = -2;
-          if (row <= kv_hi)
-            for (int rr = 0; rr < a.top_k; ++rr) {
-              int gg = a.groups[(int64_t)kpos_reg * a.top_k + rr];
-              if (gg < grp && c < kMaxLow) klow_reg[c++] = gg;
-            }
-        }
+        ireg = row <= kv_hi ? a.kinfo[row] : i32x4_t{0x7fffffff, -1, -1, -1};
       }
     }
   };
@@ -320,28 +314,32 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
     }
     if constexpr (GROUP) {
       if (tid < KT) {
-        sm.kpos[tid] = kpos_reg;
-        for (int c = 0; c < kMaxLow; ++c) sm.klow[tid * kMaxLow + c] = klow_reg[c];
+        sm.kpos[tid] = ireg[0];
+#pragma unroll
+        for (int c = 0; c < NLOW; ++c) sm.klow[c][tid] = ireg[1 + c];
       }
     }
     __syncthreads();
     if (it + 1 < ntiles) load_tile(ks + KT);
 
-    // ------------------------------------------------------------ per-wave skip / mask decision
+    // ------------------------------------------------------------ tile class for this wave
     if (!wave_active) continue;
     const int64_t k_last = ks + KT - 1;
-    bool skip, full;
+    int cls;
     if constexpr (GROUP) {
-      const int kpos_first = sm.kpos[0];
-      const int kpos_last = k_last <= kv_hi ? sm.kpos[KT - 1] : 0x7fffffff;
-      skip = ks > wq_hi || (int64_t)wpos_hi - kpos_first < a.window;
-      full = k_last <= kv_hi && k_last <= wq_lo && (int64_t)wpos_lo - kpos_last >= a.window &&
-             a.top_k == 1;
+      const bool whole = k_last <= kv_hi;
+      const int kp_first = sm.kpos[0];
+      const int kp_last = whole ? sm.kpos[KT - 1] : 0x7fffffff;
+      if (ks > wq_hi || (int64_t)wpos_hi - kp_first < a.window) cls = kSkip;
+      else if (whole && k_last <= wq_lo && (int64_t)wpos_lo - kp_last >= a.window)
+        cls = NLOW == 0 ? kFull : kFar;
+      else cls = kEdge;
     } else {
-      skip = ks > wq_hi || wq_lo - k_last >= a.window;
-      full = k_last <= wq_lo && wq_hi - ks < a.window;
+      if (ks > wq_hi || wq_lo - k_last >= a.window) cls = kSkip;
+      else if (k_last <= wq_lo && wq_hi - ks < a.window) cls = kFull;
+      else cls = kEdge;
     }
-    if (skip) continue;
+    if (cls == kSkip) continue;
 
     // ------------------------------------------------------------ S^T = K Q^T
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
@@ -354,40 +352,58 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
       }
     }
 
-    // ------------------------------------------------------------ mask + online softmax
-    // element v of tile kb holds key kb*32 + 8*(v/4) + 4*hg + v%4 of this tile
+    // ------------------------------------------------------------ mask
+    // accumulator element v of tile kb is key kb*32 + 8*(v/4) + 4*hg + v%4 of this tile: four
+    // consecutive keys per group of four elements, read from LDS as one 16-byte vector
+    if (cls != kFull) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kk0 = kb * 32 + 8 * q4 + 4 * hg;
+          bool ok[4] = {true, true, true, true};
+          if constexpr (GROUP) {
+            if (cls == kEdge) {
+              const i32x4_t kp = *(const i32x4_t*)&sm.kpos[kk0];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ok[e] = (int64_t)qpos - kp[e] >= a.window;
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < NLOW; ++c2) {
+              const i32x4_t kl = *(const i32x4_t*)&sm.klow[c2][kk0];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c1 = 0; c1 < NLOW; ++c1) ok[e] = ok[e] && kl[e] != qlow[c1];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t d = qi - (ks + kk0 + e);
+              ok[e] = d >= 0 && d < a.window;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!ok[e]) sacc[kb][4 * q4 + e] = -INFINITY;
+        }
+    }
+
+    // ------------------------------------------------------------ online softmax
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int vi = 0; vi < 16; ++vi) {
-        float x = sacc[kb][vi] * a.sl2;
-        if (!full) {
-          const int kk = kb * 32 + 8 * (vi >> 2) + 4 * hg + (vi & 3);
-          const int64_t kidx = ks + kk;
-          bool ok;
-          if constexpr (GROUP) {
-            const int kp = sm.kpos[kk];
-            ok = qvalid && kidx <= qi && (int64_t)qpos - kp >= a.window;
-            if (a.top_k > 1) {
-#pragma unroll
-              for (int c1 = 0; c1 < kMaxLow; ++c1)
-#pragma unroll
-                for (int c2 = 0; c2 < kMaxLow; ++c2)
-                  ok = ok && !(qlow[c1] == sm.klow[kk * kMaxLow + c2]);
-            }
-          } else {
-            ok = qvalid && kidx <= qi && qi - kidx < a.window;
-          }
-          x = ok ? x : -INFINITY;
-        }
-        sacc[kb][vi] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+      for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.sl2;
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    if (__any(m_new > m_run)) {  // rescale only when some row's running max moved
+      const float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+    }
     m_run = m_new;
     float psum = 0.f;
     bf16x8_t pb[4];
@@ -395,13 +411,11 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int vi = 0; vi < 16; ++vi) {
-        float p = fast_exp2(sacc[kb][vi] - m_use);
+        const float p = fast_exp2(sacc[kb][vi] * a.sl2 - m_use);
         psum += p;
         pb[kb * 2 + (vi >> 3)][vi & 7] = to_bf16(p);
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+    l_run += psum;
 
     // ------------------------------------------------------------ O^T += V^T P^T
 #pragma unroll
@@ -435,20 +449,18 @@ __global__ __launch_bounds__(256) void flash_kernel(const FlashArgs a) {
     a.lse[qi * a.Hq + hq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <bool GROUP>
-static hipError_t flash_launch(const FlashArgs& fa, int dh, int64_t blocks, hipStream_t stream) {
-  if (blocks <= 0) return hipSuccess;
+template <bool GROUP, int NLOW>
+static void flash_dispatch_dh(const FlashArgs& fa, int dh, int64_t blocks, hipStream_t stream) {
   if (dh == 128)
-    hipLaunchKernelGGL((flash_kernel<128, GROUP>), dim3(blocks), dim3(256), 0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW>), dim3(blocks), dim3(256), 0, stream, fa);
   else
-    hipLaunchKernelGGL((flash_kernel<64, GROUP>), dim3(blocks), dim3(256), 0, stream, fa);
-  return hipGetLastError();
+    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW>), dim3(blocks), dim3(256), 0, stream, fa);
 }
 
 hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const uint16_t* vg,
                                   const int32_t* offsets, const int32_t* tile_pre,
-                                  const int32_t* idx, const int32_t* groups, const AttnShape& s,
-                                  float* og, float* lseg, hipStream_t stream) {
+                                  const int32_t* kinfo, const AttnShape& s, float* og, float* lseg,
+                                  hipStream_t stream) {
   FlashArgs fa{};
   fa.q = qg;
   fa.k = kg;
@@ -464,13 +476,19 @@ hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const 
   fa.sl2 = s.scale * kLog2e;
   fa.seg_off = offsets;
   fa.tile_pre = tile_pre;
-  fa.pos = idx;
-  fa.groups = groups;
+  fa.kinfo = (const i32x4_t*)kinfo;
   fa.K = s.K;
-  fa.top_k = s.top_k;
   // upper bound on the tiles of all segments: sum of ceil(size / T) <= ceil(nk / T) + K
-  int64_t w_max = (s.nk + fa.T - 1) / fa.T + s.K;
-  return flash_launch<true>(fa, s.dh, xcd_grid((int64_t)s.Hkv * w_max), stream);
+  const int64_t w_max = (s.nk + fa.T - 1) / fa.T + s.K;
+  const int64_t blocks = xcd_grid((int64_t)s.Hkv * w_max);
+  if (blocks <= 0) return hipSuccess;
+  switch (s.top_k) {
+    case 1: flash_dispatch_dh<true, 0>(fa, s.dh, blocks, stream); break;
+    case 2: flash_dispatch_dh<true, 1>(fa, s.dh, blocks, stream); break;
+    case 3: flash_dispatch_dh<true, 2>(fa, s.dh, blocks, stream); break;
+    default: flash_dispatch_dh<true, 3>(fa, s.dh, blocks, stream); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -490,7 +508,10 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
   fa.window = s.window;
   fa.sl2 = s.scale * kLog2e;
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
-  return flash_launch<false>(fa, s.dh, xcd_grid((int64_t)s.Hkv * fa.tiles_per_head), stream);
+  const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
+  if (blocks <= 0) return hipSuccess;
+  flash_dispatch_dh<false, 0>(fa, s.dh, blocks, stream);
+  return hipGetLastError();
 }
 
 // ============================================================================ merge

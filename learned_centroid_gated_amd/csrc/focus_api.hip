@@ -68,6 +68,7 @@ struct AttnWs {
   uint16_t *qg, *kg, *vg;
   float *og, *lseg, *ol, *lsel;
   int32_t* tile_pre;
+  int32_t* kinfo;
 };
 
 size_t attn_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k, AttnWs* out) {
@@ -82,6 +83,7 @@ size_t attn_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k
   w.ol = c.take<float>((size_t)n * Hq * dh);
   w.lsel = c.take<float>((size_t)n * Hq);
   w.tile_pre = c.take<int32_t>((size_t)K + 1);
+  w.kinfo = c.take<int32_t>((size_t)nk * 4);
   if (out) *out = w;
   return c.used;
 }
@@ -251,15 +253,16 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     return hipEventRecord((hipEvent_t)stage_events[i], st);
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_gather_qkv(q, k, v, idx, s, w.qg, w.kg, w.vg, st);
+  if (e == hipSuccess)
+    e = launch_gather_qkv(q, k, v, idx, groups, slot, s, w.qg, w.kg, w.vg, w.kinfo, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_tile_prefix(offsets, K, attn_tile_tokens(s.G), w.tile_pre, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
-    e = launch_group_attention(w.qg, w.kg, w.vg, offsets, w.tile_pre, idx, groups, s, w.og,
-                               w.lseg, st);
+    e = launch_group_attention(w.qg, w.kg, w.vg, offsets, w.tile_pre, w.kinfo, s, w.og, w.lseg,
+                               st);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess) e = launch_window_attention(q, k, v, s, w.ol, w.lsel, st);

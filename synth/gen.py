@@ -104,13 +104,16 @@ def assign_inputs(n, d, dg, K, mix, weights="uniform", noise_frac=0.0, sigma=0.5
 
 
 # ---------------------------------------------------------------- attention inputs
-def qkv_inputs(n, Hq, Hkv, dh, index=0, salt=0, device="cpu", lead=()):
+def qkv_inputs(n, Hq, Hkv, dh, index=0, salt=0, device="cpu", lead=(), which="qkv"):
     """Q [*lead, n, Hq, dh], K and V [*lead, n, Hkv, dh], N(0,1) rounded to bf16.
 
     device="cpu": numpy uint16 bf16 bit patterns. device="cuda": torch bfloat16 on cuda:0.
+    `which` selects the tensors to draw (each has its own stream, so a subset draws the same
+    values as the full set).
     """
     lead = tuple(lead)
     shapes = {"q": lead + (n, Hq, dh), "k": lead + (n, Hkv, dh), "v": lead + (n, Hkv, dh)}
+    shapes = {x: shp for x, shp in shapes.items() if x in which}
     if device == "cpu":
         rs = seed_streams(index, salt)
         return {name: f32_to_bf16_bits(rs[name].standard_normal(shp, dtype=np.float32))
@@ -120,7 +123,14 @@ def qkv_inputs(n, Hq, Hkv, dh, index=0, salt=0, device="cpu", lead=()):
     for name, shp in shapes.items():
         g = torch.Generator(device="cuda")
         g.manual_seed(_stream_seed(index, salt, name))
-        out[name] = torch.randn(shp, dtype=torch.float32, device="cuda", generator=g).to(torch.bfloat16)
+        t = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
+        flat = t.view(-1, shp[-2] * shp[-1])
+        rows = max(1, (1 << 28) // flat.shape[1])  # fp32 temporaries of at most 1 GiB
+        for r0 in range(0, flat.shape[0], rows):
+            r1 = min(flat.shape[0], r0 + rows)
+            flat[r0:r1] = torch.randn((r1 - r0, flat.shape[1]), dtype=torch.float32, device="cuda",
+                                      generator=g).to(torch.bfloat16)
+        out[name] = t
     return out
 
 
@@ -135,6 +145,10 @@ def random_groups(n, K, top_k, rng, skew=0.0):
     if top_k == 1:
         out[:, 0] = rng.choice(K, size=n, p=w)
         return out
-    for i in range(n):
-        out[i] = np.sort(rng.choice(K, size=top_k, replace=False, p=w))
+    # weighted sampling without replacement: the top_k of log(w) + Gumbel noise per token
+    logw = np.log(w)[None, :]
+    for r0 in range(0, n, 65536):
+        r1 = min(n, r0 + 65536)
+        keys = logw + rng.gumbel(size=(r1 - r0, K))
+        out[r0:r1] = np.sort(np.argpartition(-keys, top_k - 1, axis=1)[:, :top_k], axis=1)
     return out
