@@ -143,7 +143,7 @@ struct FlashArgs {
   float* lse;         // [rows, Hq] natural-log sum of exp of the scaled logits (-inf if none)
   int64_t n;          // window: tokens
   int Hq, Hkv, G, T;
-  int64_t window;
+  int window;         // clamped to n: a window of n tokens already spans every causal pair
   float sl2;          // scale * log2(e)
   const int32_t* seg_off;   // group: [K+1]
   const int32_t* tile_pre;  // group: [K+1]
@@ -176,6 +176,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   constexpr int RPP = 256 / CH;     // K rows per load pass
   constexpr int KPASS = KT / RPP;   // K load passes
   constexpr int VKPT = DH / 32;     // V keys per thread (transposed store)
+  constexpr int VG = KT / VKPT;     // V key groups per tile
   constexpr int NS = DH / 16;       // MFMA k-steps over the head dimension
   constexpr int ND = DH / 32;       // 32-wide output tiles over the head dimension
   __shared__ __attribute__((aligned(16))) Smem sm;
@@ -188,8 +189,9 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   if (comb < 0) return;
   const int h = (int)(comb / W);
   const int item = (int)(comb - (int64_t)h * W);
+  const int window = a.window;
 
-  int64_t q0, q1, kv_lo;
+  int q0, q1, kv_lo;  // slots (group) or tokens (window); all below 2^31
   if constexpr (GROUP) {
     int lo = 0, hi = a.K - 1;  // largest g with tile_pre[g] <= item (a non-empty segment)
     while (lo < hi) {
@@ -199,27 +201,27 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     }
     const int nt = a.tile_pre[lo + 1] - a.tile_pre[lo];
     const int t = nt - 1 - (item - a.tile_pre[lo]);  // heaviest tiles of a segment first
-    const int64_t s_lo = a.seg_off[lo], s_hi = a.seg_off[lo + 1];
-    q0 = s_lo + (int64_t)t * a.T;
-    q1 = q0 + a.T < s_hi ? q0 + a.T : s_hi;
+    const int s_lo = a.seg_off[lo], s_hi = a.seg_off[lo + 1];
+    q0 = s_lo + t * a.T;
+    q1 = min(q0 + a.T, s_hi);
     kv_lo = s_lo;
   } else {
-    q0 = (int64_t)item * a.T;
-    q1 = q0 + a.T < a.n ? q0 + a.T : a.n;
-    kv_lo = q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0;
+    q0 = item * a.T;
+    q1 = (int)min((int64_t)q0 + a.T, a.n);
+    kv_lo = max(q0 - window + 1, 0);
   }
-  const int64_t kv_hi = q1 - 1;  // last key index any query of the tile may see
+  const int kv_hi = q1 - 1;  // last key index any query of the tile may see
 
   // ---------------------------------------------------------------- this lane's query row
   const int r = wave * 32 + jq;
   const int head_local = r / a.T, tok_local = r % a.T;
   const int hq = h * a.G + head_local;
-  const int64_t qi = q0 + tok_local;
+  const int qi = q0 + tok_local;
   const bool qvalid = qi < q1;
   const int wt0 = (wave * 32) % a.T;
   const int wtn = a.T < 32 ? a.T : 32;
-  const int64_t wq_lo = q0 + wt0;
-  const int64_t wq_hi = (q0 + wt0 + wtn < q1 ? q0 + wt0 + wtn : q1) - 1;
+  const int wq_lo = q0 + wt0;
+  const int wq_hi = min(q0 + wt0 + wtn, q1) - 1;
   const bool wave_active = wq_hi >= wq_lo;
 
   int qpos = 0, wpos_lo = 0, wpos_hi = 0, tpos_hi = 0;
@@ -237,30 +239,30 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     }
     tpos_hi = a.kinfo[kv_hi][0];
   } else {
-    qpos = (int)qi;
+    qpos = qi;
   }
 
   bf16x8_t qreg[NS];
   {
-    const uint16_t* qp = a.q + ((qvalid ? qi : 0) * a.Hq + hq) * (int64_t)DH + 8 * hg;
+    const uint16_t* qp = a.q + ((int64_t)(qvalid ? qi : 0) * a.Hq + hq) * DH + 8 * hg;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qreg[s] = qvalid ? *(const bf16x8_t*)(qp + 16 * s) : bf16x8_t{};
   }
 
   // ---------------------------------------------------------------- kv tile range
-  int64_t ntiles;
+  int ntiles;
   if constexpr (GROUP) {
     // tiles up to the first one whose pairs all fall inside the window (positions ascend)
-    int64_t lo_t = 0, hi_t = (kv_hi - kv_lo) / KT + 1;
+    int lo_t = 0, hi_t = (kv_hi - kv_lo) / KT + 1;
     while (lo_t < hi_t) {
-      int64_t mid = (lo_t + hi_t) >> 1;
-      if ((int64_t)tpos_hi - a.kinfo[kv_lo + mid * KT][0] < a.window) hi_t = mid;
+      int mid = (lo_t + hi_t) >> 1;
+      if (tpos_hi - a.kinfo[kv_lo + mid * KT][0] < window) hi_t = mid;
       else lo_t = mid + 1;
     }
     ntiles = lo_t;
   } else {
-    ntiles = a.window > 0 ? (kv_hi - kv_lo) / KT + 1 : 0;
+    ntiles = window > 0 ? (kv_hi - kv_lo) / KT + 1 : 0;
   }
 
   f32x16_t oacc[ND];
@@ -268,48 +270,54 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // K: thread (kc, kr) loads 16-byte chunk kc of rows kr + p*RPP.
+  // V: lanes of one wave cover the 16 key groups of a chunk, so each 16-lane phase of the
+  // transposed LDS store hits 16 distinct 8-byte bank pairs.
   bf16x8_t kreg[KPASS];
   bf16x8_t vreg[VKPT];
   i32x4_t ireg = {0x7fffffff, -1, -1, -1};
-  const int lc = tid % CH, lr = tid / CH;
-  const int64_t kstride = (int64_t)a.Hkv * DH;
-  const uint16_t* kbase = a.k + (int64_t)h * DH + lc * 8;
-  const uint16_t* vbase = a.v + (int64_t)h * DH + lc * 8;
+  const int kc = tid % CH, kr = tid / CH;
+  const int vgrp = tid % VG, vc = tid / VG;  // key group (VKPT keys) and 16-byte chunk
+  const uint32_t kstride = (uint32_t)a.Hkv * DH;  // elements between consecutive rows
+  const uint16_t* khead = a.k + (int64_t)h * DH;
+  const uint16_t* vhead = a.v + (int64_t)h * DH;
 
-  auto load_tile = [&](int64_t ks) {
+  auto load_tile = [&](int ks) {
+    const uint16_t* kb = khead + (int64_t)ks * kstride;  // uniform tile base
+    const uint16_t* vb = vhead + (int64_t)ks * kstride;
+    const int nrow = kv_hi - ks;  // rows 0..nrow of the tile are valid
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      int64_t row = ks + lr + p * RPP;
-      kreg[p] = row <= kv_hi ? *(const bf16x8_t*)(kbase + row * kstride) : bf16x8_t{};
+      const int row = kr + p * RPP;
+      kreg[p] = row <= nrow ? *(const bf16x8_t*)(kb + (uint32_t)row * kstride + kc * 8)
+                            : bf16x8_t{};
     }
 #pragma unroll
     for (int e = 0; e < VKPT; ++e) {
-      int64_t row = ks + lr * VKPT + e;
-      vreg[e] = row <= kv_hi ? *(const bf16x8_t*)(vbase + row * kstride) : bf16x8_t{};
+      const int row = vgrp * VKPT + e;
+      vreg[e] = row <= nrow ? *(const bf16x8_t*)(vb + (uint32_t)row * kstride + vc * 8)
+                            : bf16x8_t{};
     }
     if constexpr (GROUP) {
-      if (tid < KT) {
-        int64_t row = ks + tid;
-        ireg = row <= kv_hi ? a.kinfo[row] : i32x4_t{0x7fffffff, -1, -1, -1};
-      }
+      if (tid < KT) ireg = tid <= nrow ? a.kinfo[ks + tid] : i32x4_t{0x7fffffff, -1, -1, -1};
     }
   };
 
   if (ntiles > 0) load_tile(kv_lo);
-  for (int64_t it = 0; it < ntiles; ++it) {
-    const int64_t ks = kv_lo + it * KT;
+  for (int it = 0; it < ntiles; ++it) {
+    const int ks = kv_lo + it * KT;
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) *(bf16x8_t*)&sm.k[(lr + p * RPP) * KS + lc * 8] = kreg[p];
+    for (int p = 0; p < KPASS; ++p) *(bf16x8_t*)&sm.k[(kr + p * RPP) * KS + kc * 8] = kreg[p];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if constexpr (VKPT == 4) {
         bf16x4_t t4 = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *(bf16x4_t*)&sm.vt[(lc * 8 + e) * VS + lr * 4] = t4;
+        *(bf16x4_t*)&sm.vt[(vc * 8 + e) * VS + vgrp * 4] = t4;
       } else {
         typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
         bf16x2_t t2 = {vreg[0][e], vreg[1][e]};
-        *(bf16x2_t*)&sm.vt[(lc * 8 + e) * VS + lr * 2] = t2;
+        *(bf16x2_t*)&sm.vt[(vc * 8 + e) * VS + vgrp * 2] = t2;
       }
     }
     if constexpr (GROUP) {
@@ -324,19 +332,19 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
     // ------------------------------------------------------------ tile class for this wave
     if (!wave_active) continue;
-    const int64_t k_last = ks + KT - 1;
+    const int k_last = ks + KT - 1;
     int cls;
     if constexpr (GROUP) {
       const bool whole = k_last <= kv_hi;
       const int kp_first = sm.kpos[0];
       const int kp_last = whole ? sm.kpos[KT - 1] : 0x7fffffff;
-      if (ks > wq_hi || (int64_t)wpos_hi - kp_first < a.window) cls = kSkip;
-      else if (whole && k_last <= wq_lo && (int64_t)wpos_lo - kp_last >= a.window)
+      if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
+      else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
         cls = NLOW == 0 ? kFull : kFar;
       else cls = kEdge;
     } else {
-      if (ks > wq_hi || wq_lo - k_last >= a.window) cls = kSkip;
-      else if (k_last <= wq_lo && wq_hi - ks < a.window) cls = kFull;
+      if (ks > wq_hi || wq_lo - k_last >= window) cls = kSkip;
+      else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
       else cls = kEdge;
     }
     if (cls == kSkip) continue;
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
             if (cls == kEdge) {
               const i32x4_t kp = *(const i32x4_t*)&sm.kpos[kk0];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) ok[e] = (int64_t)qpos - kp[e] >= a.window;
+              for (int e = 0; e < 4; ++e) ok[e] = qpos - kp[e] >= window;
             }
 #pragma unroll
             for (int c2 = 0; c2 < NLOW; ++c2) {
@@ -379,8 +387,8 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int64_t d = qi - (ks + kk0 + e);
-              ok[e] = d >= 0 && d < a.window;
+              const int d = qi - (ks + kk0 + e);
+              ok[e] = d >= 0 && d < window;
             }
           }
 #pragma unroll
@@ -411,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int vi = 0; vi < 16; ++vi) {
-        const float p = fast_exp2(sacc[kb][vi] * a.sl2 - m_use);
+        const float p = fast_exp2(__builtin_fmaf(sacc[kb][vi], a.sl2, -m_use));
         psum += p;
         pb[kb * 2 + (vi >> 3)][vi & 7] = to_bf16(p);
       }
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   if (!qvalid) return;
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  float* op = a.o + (qi * a.Hq + hq) * (int64_t)DH;
+  float* op = a.o + ((int64_t)qi * a.Hq + hq) * DH;
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       *(f32x4_t*)(op + d * 32 + g4 * 8 + 4 * hg) = x;
     }
   if (hg == 0)
-    a.lse[qi * a.Hq + hq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    a.lse[(int64_t)qi * a.Hq + hq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <bool GROUP, int NLOW>
@@ -472,7 +480,7 @@ hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const 
   fa.Hkv = s.Hkv;
   fa.G = s.G;
   fa.T = attn_tile_tokens(s.G);
-  fa.window = s.window;
+  fa.window = (int)(s.window < s.n ? s.window : s.n);
   fa.sl2 = s.scale * kLog2e;
   fa.seg_off = offsets;
   fa.tile_pre = tile_pre;
@@ -505,7 +513,7 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
   fa.Hkv = s.Hkv;
   fa.G = s.G;
   fa.T = attn_tile_tokens(s.G);
-  fa.window = s.window;
+  fa.window = (int)(s.window < s.n ? s.window : s.n);
   fa.sl2 = s.scale * kLog2e;
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
