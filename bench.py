@@ -3,7 +3,7 @@
 
 A step is one pass of the prefill hot path over one synthetic sequence with every input already
 resident in HBM: focus_assign (scores, Sinkhorn, top-k) -> focus_bucket -> focus_attention
-(gather, group pass, window pass, merge). The headline line is the 128K-token 70B-shaped GQA
+(gather, group pass, window pass with the merge in its epilogue). The headline line is the 128K-token 70B-shaped GQA
 layer; the 1M-token prefill, the batched decode and a dense causal baseline on the same GPU are
 reported beside it. Kernel times inside focus_attention come from HIP events the library records
 on its own stream around each stage (focus_attention_ex).
@@ -34,7 +34,7 @@ METRIC = "Focus prefill tokens/s/GPU at 128K & 1M; attn TFLOP/s as % of bf16 MFM
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-STAGES = ("gather", "tile_prefix", "group_attention", "window_attention", "merge")
+STAGES = ("gather", "tile_prefix", "group_attention", "window_attention_merge")
 
 
 def log(*a):
@@ -66,11 +66,11 @@ class Hip:
 
 def attention_ex(hip, q, k, v, groups, off, idx, slot, K, window, out, lse, ws, events):
     n, Hq, dh = q.shape
-    arr = (ctypes.c_void_p * 10)(*events)
+    arr = (ctypes.c_void_p * 8)(*events)
     _lib.call("focus_attention_ex", q.data_ptr(), k.data_ptr(), v.data_ptr(), n, Hq, k.shape[1], dh,
               groups.data_ptr(), off.data_ptr(), idx.data_ptr(), slot.data_ptr(), K,
               groups.shape[1], int(window), 0.0, out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
-              ws.numel(), torch.cuda.current_stream().cuda_stream, arr, 10)
+              ws.numel(), torch.cuda.current_stream().cuda_stream, arr, 8)
 
 
 # ------------------------------------------------------------------ prefill
@@ -79,13 +79,13 @@ def window_pairs(n, w):
     return int(np.minimum(i + 1, w).sum())
 
 
-def count_allowed_pairs(k, v, groups, off, idx, slot, K, window):
+def count_allowed_pairs(q, k, v, groups, off, idx, slot, K, window):
     """Exact allowed-pair count from the product path's Q = 0 run: every logit is 0, so
-    exp(lse_i) is the number of keys row i attends (the tests pin this against the oracle)."""
-    n = k.shape[0]
-    q0 = torch.zeros((n, 1, k.shape[2]), dtype=torch.bfloat16, device="cuda")
-    k1, v1 = k[:, :1].contiguous(), v[:, :1].contiguous()
-    _, lse = focus_attention(q0, k1, v1, groups, off, idx, slot, K, window)
+    exp(lse_i) is the number of keys row i attends (the tests pin this against the oracle).
+    The run uses the benchmarked shapes, so its kernels match the timed ones."""
+    q0 = torch.zeros_like(q)
+    _, lse = focus_attention(q0, k, v, groups, off, idx, slot, K, window)
+    del q0
     counts = torch.exp(lse[:, 0].double()).round().to(torch.int64)
     return int(counts.sum().item())
 
@@ -115,7 +115,7 @@ def prefill_bench(c, steps, warmup, hip):
     log(f"[bench]   inputs resident in {time.time() - t0:.1f}s; workspaces "
         f"{(ws_a.numel() + ws_b.numel() + ws_t.numel()) / 2**30:.1f} GiB")
 
-    stage_ev = [[hip.event() for _ in range(10)] for _ in range(steps)]
+    stage_ev = [[hip.event() for _ in range(8)] for _ in range(steps)]
     call_ev = [[hip.event() for _ in range(3)] for _ in range(steps)]
     rec = hip.h.hipEventRecord
     rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -132,7 +132,7 @@ def prefill_bench(c, steps, warmup, hip):
         if i is not None:
             rec(call_ev[i][2], stream)
         attention_ex(hip, q, k, v, groups, off, idx, slot, c.K, c.window, out, lse, ws_t,
-                     stage_ev[i] if i is not None else [None] * 10)
+                     stage_ev[i] if i is not None else [None] * 8)
 
     for _ in range(warmup):
         step()
@@ -156,7 +156,7 @@ def prefill_bench(c, steps, warmup, hip):
             hip.destroy(x)
 
     # effective FLOPs on the exact allowed-pair count (untimed accounting pass)
-    pairs = count_allowed_pairs(k, v, groups, off, idx, slot, c.K, c.window)
+    pairs = count_allowed_pairs(q, k, v, groups, off, idx, slot, c.K, c.window)
     wpairs = window_pairs(c.n, c.window)
     gpairs = pairs - wpairs
     flops_pair = 4.0 * c.dh * c.Hq
@@ -171,35 +171,32 @@ def prefill_bench(c, steps, warmup, hip):
         "density_vs_causal": pairs / (c.n * (c.n + 1) / 2),
         "segment_sizes": {"min": int(sizes.min()), "mean": float(sizes.mean()), "max": int(sizes.max())},
     }
-    attn_ms = stage_ms["group_attention"] + stage_ms["window_attention"]
+    attn_ms = stage_ms["group_attention"] + stage_ms["window_attention_merge"]
     res["attention_tflops"] = flops_pair * pairs / (attn_ms * 1e-3) / 1e12
     res["attention_pct_bf16_peak"] = 100 * res["attention_tflops"] / PEAK_BF16_TFLOPS
     res["group_tflops"] = flops_pair * gpairs / (stage_ms["group_attention"] * 1e-3) / 1e12
-    res["window_tflops"] = flops_pair * wpairs / (stage_ms["window_attention"] * 1e-3) / 1e12
-    # algorithmic bytes of the HBM-bound stages
-    bpe = 2  # bf16
-    gather_bytes = nk * (c.Hq + 2 * c.Hkv) * c.dh * bpe * 2          # read + write per membership
-    merge_bytes = c.n * c.Hq * (c.dh * 4 + 4) * (1 + c.top_k) + c.n * c.Hq * (c.dh * bpe + 4)
+    res["window_merge_tflops"] = flops_pair * wpairs / (stage_ms["window_attention_merge"] * 1e-3) / 1e12
+    # algorithmic bytes of the HBM-bound gather: K and V rows read and written per membership,
+    # plus the 16-byte key record written per membership
+    gather_bytes = nk * (2 * c.Hkv * c.dh * 2 * 2 + 16)
     res["gather_GBs"] = gather_bytes / (stage_ms["gather"] * 1e-3) / 1e9
-    res["merge_GBs"] = merge_bytes / (stage_ms["merge"] * 1e-3) / 1e9
-    assign_flops = 2.0 * c.n * c.d * (c.K if c.d * c.K <= c.d * c.dg + c.dg * c.K else c.dg) + \
-        (0 if c.d * c.K <= c.d * c.dg + c.dg * c.K else 2.0 * c.n * c.dg * c.K)
+    fold = c.d * c.K <= c.d * c.dg + c.dg * c.K
+    assign_flops = 2.0 * c.n * c.d * c.K if fold else 2.0 * c.n * (c.d * c.dg + c.dg * c.K)
     res["assign_fp32_tflops"] = assign_flops / (assign_ms * 1e-3) / 1e12
     res["assign_hidden_GBs"] = c.n * c.d * 4 / (assign_ms * 1e-3) / 1e9
     # the dominant kernel of the step
-    dom = max(("group_attention", "window_attention", "gather", "merge"), key=lambda s: stage_ms[s])
-    if dom in ("group_attention", "window_attention"):
+    dom = max(("group_attention", "window_attention_merge", "gather"), key=lambda s: stage_ms[s])
+    if dom != "gather":
         p = gpairs if dom == "group_attention" else wpairs
         ach = flops_pair * p / (stage_ms[dom] * 1e-3) / 1e12
         res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                           "algorithmic_per_launch": flops_pair * p}
+                           "algorithmic_per_launch": flops_pair * p, "avg_launch_ms": stage_ms[dom]}
     else:
-        b = gather_bytes if dom == "gather" else merge_bytes
-        ach = b / (stage_ms[dom] * 1e-3) / 1e9
+        ach = gather_bytes / (stage_ms[dom] * 1e-3) / 1e9
         res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
-                           "algorithmic_per_launch": b}
+                           "algorithmic_per_launch": gather_bytes, "avg_launch_ms": stage_ms[dom]}
     log(f"[bench]   {ms:.3f} ms/step  {res['tokens_per_s']:.4g} tok/s  stages {stage_ms} "
         f"assign {assign_ms:.3f} bucket {bucket_ms:.3f}")
     state = dict(q=q, k=k, v=v, groups=groups, off=off, idx=idx, slot=slot, out=out, lse=lse,
@@ -213,14 +210,14 @@ def dense_baseline(c, st, hip, reps=2):
     scaled_dot_product_attention(is_causal=True) on the same Q/K/V."""
     q, k, v = st["q"], st["k"], st["v"]
     out, lse, ws = st["out"], st["lse"], st["ws_t"]
-    ev = [hip.event() for _ in range(10)]
+    ev = [hip.event() for _ in range(8)]
     times = []
     for r in range(reps + 1):
         attention_ex(hip, q, k, v, st["groups"], st["off"], st["idx"], st["slot"], c.K, c.n, out,
                      lse, ws, ev)
         torch.cuda.synchronize()
         if r:
-            times.append(hip.elapsed_ms(ev[6], ev[7]))
+            times.append(hip.elapsed_ms(ev[6], ev[7]))  # window attention with merge
     for e in ev:
         hip.destroy(e)
     own_ms = float(np.mean(times))

@@ -142,11 +142,12 @@ int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Same as focus_attention, and in addition records caller-created hipEvent_t handles on
- * `stream` around each of its five kernels, for benchmarks that time one stage:
+ * `stream` around each of its four kernels, for benchmarks that time one stage:
  * stage_events[2 s] just before and stage_events[2 s + 1] just after stage s, with
- * s = 0 gather of Q/K/V into group segments, 1 tile prefix, 2 group attention,
- * 3 window attention, 4 log-sum-exp merge. NULL entries are skipped; num_events is the
- * length of the array (0 to 10). Event-record failures return FOCUS_ERR_HIP. */
+ * s = 0 gather of K/V and per-membership key records into group segments, 1 tile prefix,
+ * 2 group attention, 3 window attention (whose epilogue merges the group partials by
+ * log-sum-exp and writes out/lse in token order). NULL entries are skipped; num_events is
+ * the length of the array (0 to 8). Event-record failures return FOCUS_ERR_HIP. */
 int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        int64_t n, int Hq, int Hkv, int d_head,
                        const int32_t* groups, const int32_t* offsets, const int32_t* idx,

@@ -5,8 +5,10 @@
 // query i attends key j <= i when i - j < window or the tokens share a group, with an exact
 // softmax over the allowed pairs. The pairs are split between two passes so each is counted
 // once: the window pass owns i - j < window; a far pair belongs to the lowest group the two
-// tokens share. The group pass runs on contiguous group segments (gathered Q/K/V); the merge
-// combines the window part and the group parts by their log-sum-exp.
+// tokens share. The group pass runs on contiguous group segments (K/V gathered per
+// membership, Q rows read in place) and leaves one fp16 partial per membership; the window
+// pass runs in original token order and merges those partials into its own by their
+// log-sum-exp in its epilogue, writing the output back in token order.
 //
 // Flash kernel layout (both passes). A workgroup has 4 waves and 128 query rows: T = 128/G
 // tokens times the G query heads of one kv head, so K/V tiles in LDS serve all G heads. A kv
@@ -23,21 +25,20 @@ namespace focus {
 int attn_tile_tokens(int G) { return 128 / G; }
 
 // ============================================================================ gather
-// qg[s] = q[idx[s]], kg[s] = k[idx[s]], vg[s] = v[idx[s]] for every membership slot s, and
-// kinfo[s] = (token position, the token's groups below this segment's group, -1 padded): the
-// pair rule of the group pass needs only these, so its inner loop makes no dependent loads.
-__global__ __launch_bounds__(256) void gather_qkv_kernel(const i32x4_t* __restrict__ q,
-                                                         const i32x4_t* __restrict__ k,
-                                                         const i32x4_t* __restrict__ v,
-                                                         const int32_t* __restrict__ idx,
-                                                         const int32_t* __restrict__ groups,
-                                                         const int32_t* __restrict__ slot,
-                                                         int top_k, int64_t nk, int cq, int ckv,
-                                                         i32x4_t* __restrict__ qg,
-                                                         i32x4_t* __restrict__ kg,
-                                                         i32x4_t* __restrict__ vg,
-                                                         i32x4_t* __restrict__ kinfo) {
-  const int per = cq + 2 * ckv;  // 16-byte chunks per slot
+// kg[s] = k[idx[s]], vg[s] = v[idx[s]] for every membership slot s, and kinfo[s] = (token
+// position, the token's groups below this segment's group, -1 padded): the pair rule of the
+// group pass needs only these, so its inner loop makes no dependent loads. Q is not gathered:
+// each query row is read once, in place, by the group pass.
+__global__ __launch_bounds__(256) void gather_kv_kernel(const i32x4_t* __restrict__ k,
+                                                        const i32x4_t* __restrict__ v,
+                                                        const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ groups,
+                                                        const int32_t* __restrict__ slot,
+                                                        int top_k, int64_t nk, int ckv,
+                                                        i32x4_t* __restrict__ kg,
+                                                        i32x4_t* __restrict__ vg,
+                                                        i32x4_t* __restrict__ kinfo) {
+  const int per = 2 * ckv;  // 16-byte chunks per slot
   const int64_t total = nk * per;
   const int64_t stride = (int64_t)gridDim.x * 256 * 4;
   for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void gather_qkv_kernel(const i32x4_t* __restri
       int32_t tok = idx[s];
       if (tok < 0) continue;
       if (c == 0) {
-        // the membership's rank r among the token's (ascending) groups: lower groups come first
+        // the membership's rank r among the token's ascending groups: lower groups come first
         i32x4_t info = {tok, -1, -1, -1};
         for (int r = 0; r < top_k; ++r) {
           if (slot[(int64_t)tok * top_k + r] == (int32_t)s) {
@@ -64,43 +65,36 @@ __global__ __launch_bounds__(256) void gather_qkv_kernel(const i32x4_t* __restri
         }
         kinfo[s] = info;
       }
-      if (c < cq) {
-        val[u] = q[(int64_t)tok * cq + c];
-        dst[u] = s * cq + c;
-        which[u] = 0;
-      } else if (c < cq + ckv) {
-        c -= cq;
+      if (c < ckv) {
         val[u] = k[(int64_t)tok * ckv + c];
         dst[u] = s * ckv + c;
-        which[u] = 1;
+        which[u] = 0;
       } else {
-        c -= cq + ckv;
+        c -= ckv;
         val[u] = v[(int64_t)tok * ckv + c];
         dst[u] = s * ckv + c;
-        which[u] = 2;
+        which[u] = 1;
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (which[u] == 0) qg[dst[u]] = val[u];
-      else if (which[u] == 1) kg[dst[u]] = val[u];
-      else if (which[u] == 2) vg[dst[u]] = val[u];
+      if (which[u] == 0) kg[dst[u]] = val[u];
+      else if (which[u] == 1) vg[dst[u]] = val[u];
     }
   }
 }
 
-hipError_t launch_gather_qkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             const int32_t* idx, const int32_t* groups, const int32_t* slot,
-                             const AttnShape& s, uint16_t* qg, uint16_t* kg, uint16_t* vg,
-                             int32_t* kinfo, hipStream_t stream) {
-  const int cq = s.Hq * s.dh / 8, ckv = s.Hkv * s.dh / 8;
-  int64_t total = s.nk * (cq + 2 * ckv);
+hipError_t launch_gather_kv(const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                            const int32_t* groups, const int32_t* slot, const AttnShape& s,
+                            uint16_t* kg, uint16_t* vg, int32_t* kinfo, hipStream_t stream) {
+  const int ckv = s.Hkv * s.dh / 8;
+  int64_t total = s.nk * 2 * ckv;
   int64_t blocks = (total + 1023) / 1024;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(gather_qkv_kernel, dim3(blocks), dim3(256), 0, stream, (const i32x4_t*)q,
-                     (const i32x4_t*)k, (const i32x4_t*)v, idx, groups, slot, s.top_k, s.nk, cq,
-                     ckv, (i32x4_t*)qg, (i32x4_t*)kg, (i32x4_t*)vg, (i32x4_t*)kinfo);
+  hipLaunchKernelGGL(gather_kv_kernel, dim3(blocks), dim3(256), 0, stream, (const i32x4_t*)k,
+                     (const i32x4_t*)v, idx, groups, slot, s.top_k, s.nk, ckv, (i32x4_t*)kg,
+                     (i32x4_t*)vg, (i32x4_t*)kinfo);
   return hipGetLastError();
 }
 
@@ -136,12 +130,16 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int K, int T, int32_t* til
 
 // ============================================================================ flash kernel
 struct FlashArgs {
-  const uint16_t* q;  // group: gathered [nk, Hq, DH]; window: [n, Hq, DH]
-  const uint16_t* k;  // [rows, Hkv, DH]
+  const uint16_t* q;  // [n, Hq, DH] in token order (group pass: row of slot s is kinfo[s].x)
+  const uint16_t* k;  // group: gathered [nk, Hkv, DH]; window: [n, Hkv, DH]
   const uint16_t* v;
-  float* o;           // [rows, Hq, DH] normalised partial output
-  float* lse;         // [rows, Hq] natural-log sum of exp of the scaled logits (-inf if none)
-  int64_t n;          // window: tokens
+  _Float16* og;       // group pass out / window pass in: [nk, Hq, DH] normalised partials
+  float* lseg;        // group pass out / window pass in: [nk, Hq] natural log, -inf if empty
+  uint16_t* out;      // window pass: [n, Hq, DH] bf16 merged output
+  float* lse;         // window pass: [n, Hq] merged natural-log sum of exp
+  const int32_t* slot;  // window pass: [n, top_k] membership slots of each token
+  int top_k;
+  int64_t n;          // tokens
   int Hq, Hkv, G, T;
   int window;         // clamped to n: a window of n tokens already spans every causal pair
   float sl2;          // scale * log2(e)
@@ -244,7 +242,8 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
   bf16x8_t qreg[NS];
   {
-    const uint16_t* qp = a.q + ((int64_t)(qvalid ? qi : 0) * a.Hq + hq) * DH + 8 * hg;
+    const int qrow = qvalid ? (GROUP ? qpos : qi) : 0;
+    const uint16_t* qp = a.q + ((int64_t)qrow * a.Hq + hq) * DH + 8 * hg;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qreg[s] = qvalid ? *(const bf16x8_t*)(qp + 16 * s) : bf16x8_t{};
@@ -443,18 +442,74 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   // ---------------------------------------------------------------- epilogue
   if (!qvalid) return;
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  float* op = a.o + ((int64_t)qi * a.Hq + hq) * DH;
+  const float L_own = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // Oᵀ accumulator layout: lane holds dims d*32 + 8*g4 + 4*hg + 0..3 of its query row
+  if constexpr (GROUP) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    _Float16* op = a.og + ((int64_t)qi * a.Hq + hq) * DH;
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
+    for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      f32x4_t x = {oacc[d][4 * g4] * inv, oacc[d][4 * g4 + 1] * inv, oacc[d][4 * g4 + 2] * inv,
-                   oacc[d][4 * g4 + 3] * inv};
-      *(f32x4_t*)(op + d * 32 + g4 * 8 + 4 * hg) = x;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+        f16x4_t x = {(_Float16)(oacc[d][4 * g4] * inv), (_Float16)(oacc[d][4 * g4 + 1] * inv),
+                     (_Float16)(oacc[d][4 * g4 + 2] * inv), (_Float16)(oacc[d][4 * g4 + 3] * inv)};
+        *(f16x4_t*)(op + d * 32 + g4 * 8 + 4 * hg) = x;
+      }
+    if (hg == 0) a.lseg[(int64_t)qi * a.Hq + hq] = L_own;
+  } else {
+    // merge the window part with this token's group parts by log-sum-exp, in token order
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    float Lr[4];
+    int64_t srow[4];
+    float M = L_own;
+    for (int r = 0; r < a.top_k; ++r) {
+      const int sl = a.slot[(int64_t)qi * a.top_k + r];
+      srow[r] = sl;
+      Lr[r] = sl >= 0 ? a.lseg[(int64_t)sl * a.Hq + hq] : -INFINITY;
+      M = fmaxf(M, Lr[r]);
     }
-  if (hg == 0)
-    a.lse[(int64_t)qi * a.Hq + hq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    float w_own = 0.f, den = 0.f, wr[4];
+    if (M != -INFINITY) {
+      w_own = L_own == -INFINITY ? 0.f : __expf(L_own - M);
+      den = w_own;
+      for (int r = 0; r < a.top_k; ++r) {
+        wr[r] = Lr[r] == -INFINITY ? 0.f : __expf(Lr[r] - M);
+        den += wr[r];
+      }
+    }
+    const float inv_den = den > 0.f ? 1.f / den : 0.f;
+    const float c_own = l_tot > 0.f ? w_own * inv_den / l_tot : 0.f;
+    f32x4_t acc[ND][4];
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        acc[d][g4] = f32x4_t{oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2],
+                             oacc[d][4 * g4 + 3]} * c_own;
+    for (int r = 0; r < a.top_k; ++r) {
+      if (Lr[r] == -INFINITY) continue;
+      const float c = wr[r] * inv_den;
+      const _Float16* gp = a.og + (srow[r] * a.Hq + hq) * DH + 4 * hg;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f16x4_t x = *(const f16x4_t*)(gp + d * 32 + g4 * 8);
+          acc[d][g4] += c * f32x4_t{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        }
+    }
+    uint16_t* outp = a.out + ((int64_t)qi * a.Hq + hq) * DH + 4 * hg;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4_t o4 = {to_bf16(acc[d][g4][0]), to_bf16(acc[d][g4][1]), to_bf16(acc[d][g4][2]),
+                       to_bf16(acc[d][g4][3])};
+        *(bf16x4_t*)(outp + d * 32 + g4 * 8) = o4;
+      }
+    if (hg == 0) a.lse[(int64_t)qi * a.Hq + hq] = den > 0.f ? M + __logf(den) : -INFINITY;
+  }
 }
 
 template <bool GROUP, int NLOW>
@@ -465,16 +520,16 @@ static void flash_dispatch_dh(const FlashArgs& fa, int dh, int64_t blocks, hipSt
     hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW>), dim3(blocks), dim3(256), 0, stream, fa);
 }
 
-hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const uint16_t* vg,
+hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
                                   const int32_t* offsets, const int32_t* tile_pre,
-                                  const int32_t* kinfo, const AttnShape& s, float* og, float* lseg,
-                                  hipStream_t stream) {
+                                  const int32_t* kinfo, const AttnShape& s, _Float16* og,
+                                  float* lseg, hipStream_t stream) {
   FlashArgs fa{};
-  fa.q = qg;
+  fa.q = q;
   fa.k = kg;
   fa.v = vg;
-  fa.o = og;
-  fa.lse = lseg;
+  fa.og = og;
+  fa.lseg = lseg;
   fa.n = s.n;
   fa.Hq = s.Hq;
   fa.Hkv = s.Hkv;
@@ -486,6 +541,7 @@ hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const 
   fa.tile_pre = tile_pre;
   fa.kinfo = (const i32x4_t*)kinfo;
   fa.K = s.K;
+  fa.top_k = s.top_k;
   // upper bound on the tiles of all segments: sum of ceil(size / T) <= ceil(nk / T) + K
   const int64_t w_max = (s.nk + fa.T - 1) / fa.T + s.K;
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * w_max);
@@ -500,14 +556,19 @@ hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const 
 }
 
 hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   const AttnShape& s, float* ol, float* lsel,
+                                   const _Float16* og, const float* lseg, const int32_t* slot,
+                                   const AttnShape& s, uint16_t* out, float* lse,
                                    hipStream_t stream) {
   FlashArgs fa{};
   fa.q = q;
   fa.k = k;
   fa.v = v;
-  fa.o = ol;
-  fa.lse = lsel;
+  fa.og = (_Float16*)og;
+  fa.lseg = (float*)lseg;
+  fa.out = out;
+  fa.lse = lse;
+  fa.slot = slot;
+  fa.top_k = s.top_k;
   fa.n = s.n;
   fa.Hq = s.Hq;
   fa.Hkv = s.Hkv;
@@ -519,68 +580,6 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
   if (blocks <= 0) return hipSuccess;
   flash_dispatch_dh<false, 0>(fa, s.dh, blocks, stream);
-  return hipGetLastError();
-}
-
-// ============================================================================ merge
-// out[i,h] = sum_p exp(lse_p - L) * O_p over the window part and the token's group parts,
-// L = log(sum_p exp(lse_p)); lse[i,h] = L.
-template <int DH>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ol,
-                                                    const float* __restrict__ lsel,
-                                                    const float* __restrict__ og,
-                                                    const float* __restrict__ lseg,
-                                                    const int32_t* __restrict__ slot, int64_t n,
-                                                    int Hq, int top_k, uint16_t* __restrict__ out,
-                                                    float* __restrict__ lse) {
-  constexpr int TPR = DH / 4;  // threads per (token, head)
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t pair = gt / TPR;
-  const int c = (int)(gt % TPR);
-  if (pair >= n * Hq) return;
-  const int64_t i = pair / Hq;
-  const int hh = (int)(pair - i * Hq);
-  float ls[5];
-  int64_t src[5];
-  ls[0] = lsel[pair];
-  src[0] = -1;
-  float M = ls[0];
-  for (int rr = 0; rr < top_k; ++rr) {
-    int s = slot[i * top_k + rr];
-    src[rr + 1] = s;
-    ls[rr + 1] = s >= 0 ? lseg[(int64_t)s * Hq + hh] : -INFINITY;
-    M = fmaxf(M, ls[rr + 1]);
-  }
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (M != -INFINITY) {
-    for (int p = 0; p <= top_k; ++p) {
-      if (ls[p] == -INFINITY) continue;
-      float w = __expf(ls[p] - M);
-      den += w;
-      const float* op = p == 0 ? ol + pair * DH : og + (src[p] * Hq + hh) * (int64_t)DH;
-      f32x4_t x = *(const f32x4_t*)(op + 4 * c);
-      acc += w * x;
-    }
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  bf16x4_t o4 = {to_bf16(acc[0] * inv), to_bf16(acc[1] * inv), to_bf16(acc[2] * inv),
-                 to_bf16(acc[3] * inv)};
-  *(bf16x4_t*)(out + pair * DH + 4 * c) = o4;
-  if (c == 0) lse[pair] = den > 0.f ? M + __logf(den) : -INFINITY;
-}
-
-hipError_t launch_merge(const float* ol, const float* lsel, const float* og, const float* lseg,
-                        const int32_t* slot, const AttnShape& s, uint16_t* out, float* lse,
-                        hipStream_t stream) {
-  const int64_t threads = s.n * s.Hq * (s.dh / 4);
-  const int64_t blocks = (threads + 255) / 256;
-  if (s.dh == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(256), 0, stream, ol, lsel, og, lseg,
-                       slot, s.n, s.Hq, s.top_k, out, lse);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(256), 0, stream, ol, lsel, og, lseg,
-                       slot, s.n, s.Hq, s.top_k, out, lse);
   return hipGetLastError();
 }
 

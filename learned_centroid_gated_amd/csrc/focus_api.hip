@@ -65,25 +65,25 @@ size_t assign_carve(void* ws, int64_t n, int d, int d_g, int K, AssignWs* out) {
 
 // ------------------------------------------------------------------ attention plan
 struct AttnWs {
-  uint16_t *qg, *kg, *vg;
-  float *og, *lseg, *ol, *lsel;
-  int32_t* tile_pre;
+  uint16_t *kg, *vg;
+  _Float16* og;
+  float* lseg;
   int32_t* kinfo;
+  int32_t* tile_pre;
 };
 
+// Gathered K/V per membership, the per-membership key records, the group pass's fp16
+// partial outputs and their log-sum-exp, and the tile prefix of the segments.
 size_t attn_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k, AttnWs* out) {
   Carver c(ws);
   const int64_t nk = n * top_k;
   AttnWs w{};
-  w.qg = c.take<uint16_t>((size_t)nk * Hq * dh);
   w.kg = c.take<uint16_t>((size_t)nk * Hkv * dh);
   w.vg = c.take<uint16_t>((size_t)nk * Hkv * dh);
-  w.og = c.take<float>((size_t)nk * Hq * dh);
+  w.og = c.take<_Float16>((size_t)nk * Hq * dh);
   w.lseg = c.take<float>((size_t)nk * Hq);
-  w.ol = c.take<float>((size_t)n * Hq * dh);
-  w.lsel = c.take<float>((size_t)n * Hq);
-  w.tile_pre = c.take<int32_t>((size_t)K + 1);
   w.kinfo = c.take<int32_t>((size_t)nk * 4);
+  w.tile_pre = c.take<int32_t>((size_t)K + 1);
   if (out) *out = w;
   return c.used;
 }
@@ -219,7 +219,7 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        size_t workspace_bytes, void* stream, void* const* stage_events,
                        int num_events) {
   if (n < 0 || window < 0) return FOCUS_ERR_ARG;
-  if (num_events < 0 || num_events > 10 || (num_events > 0 && !stage_events)) return FOCUS_ERR_ARG;
+  if (num_events < 0 || num_events > 8 || (num_events > 0 && !stage_events)) return FOCUS_ERR_ARG;
   if (int st = check_heads(Hq, Hkv, d_head)) return st;
   if (int st = check_groups(K, top_k, 4)) return st;
   float sc;
@@ -253,23 +253,19 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     return hipEventRecord((hipEvent_t)stage_events[i], st);
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
-    e = launch_gather_qkv(q, k, v, idx, groups, slot, s, w.qg, w.kg, w.vg, w.kinfo, st);
+  if (e == hipSuccess) e = launch_gather_kv(k, v, idx, groups, slot, s, w.kg, w.vg, w.kinfo, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_tile_prefix(offsets, K, attn_tile_tokens(s.G), w.tile_pre, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
-    e = launch_group_attention(w.qg, w.kg, w.vg, offsets, w.tile_pre, w.kinfo, s, w.og, w.lseg,
-                               st);
+    e = launch_group_attention(q, w.kg, w.vg, offsets, w.tile_pre, w.kinfo, s, w.og, w.lseg, st);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
-  if (e == hipSuccess) e = launch_window_attention(q, k, v, s, w.ol, w.lsel, st);
+  if (e == hipSuccess)
+    e = launch_window_attention(q, k, v, w.og, w.lseg, slot, s, out, lse, st);
   if (e == hipSuccess) e = mark(7);
-  if (e == hipSuccess) e = mark(8);
-  if (e == hipSuccess) e = launch_merge(w.ol, w.lsel, w.og, w.lseg, slot, s, out, lse, st);
-  if (e == hipSuccess) e = mark(9);
   return hip_status(e);
 }
 

@@ -78,21 +78,19 @@ struct AttnShape {
   int64_t window;
   float scale;   // natural-units logit scale
 };
-hipError_t launch_gather_qkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             const int32_t* idx, const int32_t* groups, const int32_t* slot,
-                             const AttnShape& s, uint16_t* qg, uint16_t* kg, uint16_t* vg,
-                             int32_t* kinfo, hipStream_t stream);
+hipError_t launch_gather_kv(const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                            const int32_t* groups, const int32_t* slot, const AttnShape& s,
+                            uint16_t* kg, uint16_t* vg, int32_t* kinfo, hipStream_t stream);
 hipError_t launch_tile_prefix(const int32_t* offsets, int K, int T, int32_t* tile_pre,
                               hipStream_t stream);
-hipError_t launch_group_attention(const uint16_t* qg, const uint16_t* kg, const uint16_t* vg,
+hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
                                   const int32_t* offsets, const int32_t* tile_pre,
-                                  const int32_t* kinfo, const AttnShape& s, float* og, float* lseg,
-                                  hipStream_t stream);
+                                  const int32_t* kinfo, const AttnShape& s, _Float16* og,
+                                  float* lseg, hipStream_t stream);
 hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   const AttnShape& s, float* ol, float* lsel, hipStream_t stream);
-hipError_t launch_merge(const float* ol, const float* lsel, const float* og, const float* lseg,
-                        const int32_t* slot, const AttnShape& s, uint16_t* out, float* lse,
-                        hipStream_t stream);
+                                   const _Float16* og, const float* lseg, const int32_t* slot,
+                                   const AttnShape& s, uint16_t* out, float* lse,
+                                   hipStream_t stream);
 int attn_tile_tokens(int G);  // query tokens per attention tile: 128 / G
 
 // Decode.
