@@ -281,21 +281,30 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   const uint16_t* khead = a.k + (int64_t)h * DH;
   const uint16_t* vhead = a.v + (int64_t)h * DH;
 
+  // lane offsets of the rows this thread loads, fixed for the whole loop
+  uint32_t koff[KPASS], voff[VKPT];
+#pragma unroll
+  for (int p = 0; p < KPASS; ++p) koff[p] = (uint32_t)(kr + p * RPP) * kstride + kc * 8;
+#pragma unroll
+  for (int e = 0; e < VKPT; ++e) voff[e] = (uint32_t)(vgrp * VKPT + e) * kstride + vc * 8;
+
   auto load_tile = [&](int ks) {
     const uint16_t* kb = khead + (int64_t)ks * kstride;  // uniform tile base
     const uint16_t* vb = vhead + (int64_t)ks * kstride;
     const int nrow = kv_hi - ks;  // rows 0..nrow of the tile are valid
+    if (nrow >= KT - 1) {
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int row = kr + p * RPP;
-      kreg[p] = row <= nrow ? *(const bf16x8_t*)(kb + (uint32_t)row * kstride + kc * 8)
-                            : bf16x8_t{};
-    }
+      for (int p = 0; p < KPASS; ++p) kreg[p] = *(const bf16x8_t*)(kb + koff[p]);
 #pragma unroll
-    for (int e = 0; e < VKPT; ++e) {
-      const int row = vgrp * VKPT + e;
-      vreg[e] = row <= nrow ? *(const bf16x8_t*)(vb + (uint32_t)row * kstride + vc * 8)
-                            : bf16x8_t{};
+      for (int e = 0; e < VKPT; ++e) vreg[e] = *(const bf16x8_t*)(vb + voff[e]);
+    } else {
+      // last, partial tile: rows past the end re-read the last valid row; the mask drops them
+#pragma unroll
+      for (int p = 0; p < KPASS; ++p)
+        kreg[p] = *(const bf16x8_t*)(kb + (uint32_t)min(kr + p * RPP, nrow) * kstride + kc * 8);
+#pragma unroll
+      for (int e = 0; e < VKPT; ++e)
+        vreg[e] = *(const bf16x8_t*)(vb + (uint32_t)min(vgrp * VKPT + e, nrow) * kstride + vc * 8);
     }
     if constexpr (GROUP) {
       if (tid < KT) ireg = tid <= nrow ? a.kinfo[ks + tid] : i32x4_t{0x7fffffff, -1, -1, -1};
@@ -403,15 +412,20 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 #pragma unroll
       for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.sl2;
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    if (__any(m_new > m_run)) {  // rescale only when some row's running max moved
-      const float alpha = fast_exp2(m_run - m_use);
+    // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
+    // kLazy (log2 units), so p = exp2(x - m_ref) stays below 2^kLazy and O is rescaled on
+    // the first tile and almost never after. lse uses the same reference, so it is exact.
+    constexpr float kLazy = 8.f;
+    const bool bump = tmax > m_run + kLazy;
+    if (__any(bump)) {
+      const float m_next = bump ? tmax : m_run;
+      const float alpha = m_next == -INFINITY ? 1.f : fast_exp2(m_run - m_next);
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+      m_run = m_next;
     }
-    m_run = m_new;
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
     bf16x8_t pb[4];
 #pragma unroll
