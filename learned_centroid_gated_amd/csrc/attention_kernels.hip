@@ -152,12 +152,19 @@ struct FlashArgs {
 
 constexpr int KT = 64;  // keys per kv tile
 
+// K and V tiles live in LDS row-major, 2*DH bytes per key row, with the 16-byte chunks of row r
+// permuted by chunk ^ swz(r). swz maps the 16 rows of a block to 16 distinct values whose
+// even parts differ across any 4 consecutive rows, so both access patterns are free of bank
+// conflicts: 16 lanes reading one chunk of 16 consecutive rows (K as the MFMA A operand) and
+// 16 lanes reading 2 adjacent chunks of 4 consecutive rows (V through the transposing read).
+__device__ __forceinline__ int swz(int row) {
+  return ((row & 3) << 1) | (((row >> 2) & 1) << 3) | ((row >> 3) & 1);
+}
+
 template <int DH>
 struct FlashSmem {
-  static constexpr int KS = DH + 8;  // K tile row stride (bf16): 16 rows cover all banks
-  static constexpr int VS = KT + 4;  // transposed V row stride (bf16): 32 rows, distinct banks
-  __bf16 k[KT * KS];
-  __bf16 vt[DH * VS];
+  __bf16 k[KT * DH];
+  __bf16 v[KT * DH];
   int kpos[KT];
   int klow[3][KT];
 };
@@ -165,19 +172,18 @@ struct FlashSmem {
 // Tile classes seen by one wave.
 enum { kSkip = 0, kEdge = 1, kFar = 2, kFull = 3 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // NLOW = top_k - 1 lower groups per membership matter for the ownership rule (group pass).
 template <int DH, bool GROUP, int NLOW>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   using Smem = FlashSmem<DH>;
-  constexpr int KS = Smem::KS, VS = Smem::VS;
-  constexpr int CH = DH / 8;        // 16-byte chunks per row
-  constexpr int RPP = 256 / CH;     // K rows per load pass
-  constexpr int KPASS = KT / RPP;   // K load passes
-  constexpr int VKPT = DH / 32;     // V keys per thread (transposed store)
-  constexpr int VG = KT / VKPT;     // V key groups per tile
-  constexpr int NS = DH / 16;       // MFMA k-steps over the head dimension
-  constexpr int ND = DH / 32;       // 32-wide output tiles over the head dimension
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  constexpr int CH = DH / 8;             // 16-byte chunks per key row
+  constexpr int ROWS_PER_INST = 64 / CH; // key rows one wave-wide 1 KB LDS load covers
+  constexpr int INSTS = KT / ROWS_PER_INST / 4;  // per wave, for each of K and V
+  constexpr int NS = DH / 16;            // MFMA k-steps over the head dimension
+  constexpr int ND = DH / 32;            // 32-wide output tiles over the head dimension
+  __shared__ __attribute__((aligned(1024))) Smem smem[2];  // double buffer: one barrier per tile
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, jq = l & 31, hg = l >> 5;
 
@@ -269,187 +275,198 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // K: thread (kc, kr) loads 16-byte chunk kc of rows kr + p*RPP.
-  // V: lanes of one wave cover the 16 key groups of a chunk, so each 16-lane phase of the
-  // transposed LDS store hits 16 distinct 8-byte bank pairs.
-  bf16x8_t kreg[KPASS];
-  bf16x8_t vreg[VKPT];
-  i32x4_t ireg = {0x7fffffff, -1, -1, -1};
-  const int kc = tid % CH, kr = tid / CH;
-  const int vgrp = tid % VG, vc = tid / VG;  // key group (VKPT keys) and 16-byte chunk
-  const uint32_t kstride = (uint32_t)a.Hkv * DH;  // elements between consecutive rows
+  // ---------------------------------------------------------------- tile loads
+  // Wave w moves key rows [w*KT/4, (w+1)*KT/4) of K and of V straight into LDS with
+  // global_load_lds_dwordx4: one instruction fills 1 KB of LDS, lane L landing at byte 16*L,
+  // i.e. row L / CH of the instruction's block, swizzled position L % CH, so lane L fetches the
+  // global chunk (L % CH) ^ swz(row).
+  const uint32_t kstride = (uint32_t)a.Hkv * DH;  // elements between consecutive key rows
   const uint16_t* khead = a.k + (int64_t)h * DH;
   const uint16_t* vhead = a.v + (int64_t)h * DH;
-
-  // lane offsets of the rows this thread loads, fixed for the whole loop
-  uint32_t koff[KPASS], voff[VKPT];
+  int lrow[INSTS];
+  uint32_t loff[INSTS];
 #pragma unroll
-  for (int p = 0; p < KPASS; ++p) koff[p] = (uint32_t)(kr + p * RPP) * kstride + kc * 8;
-#pragma unroll
-  for (int e = 0; e < VKPT; ++e) voff[e] = (uint32_t)(vgrp * VKPT + e) * kstride + vc * 8;
+  for (int i = 0; i < INSTS; ++i) {
+    lrow[i] = (wave * INSTS + i) * ROWS_PER_INST + l / CH;
+    loff[i] = (uint32_t)lrow[i] * kstride + (uint32_t)(((l % CH) ^ (swz(lrow[i]) % CH)) * 8);
+  }
+  i32x4_t ireg = {0x7fffffff, -1, -1, -1};
 
-  auto load_tile = [&](int ks) {
+  auto issue_tile = [&](int ks, Smem& sb) {
     const uint16_t* kb = khead + (int64_t)ks * kstride;  // uniform tile base
     const uint16_t* vb = vhead + (int64_t)ks * kstride;
     const int nrow = kv_hi - ks;  // rows 0..nrow of the tile are valid
-    if (nrow >= KT - 1) {
 #pragma unroll
-      for (int p = 0; p < KPASS; ++p) kreg[p] = *(const bf16x8_t*)(kb + koff[p]);
-#pragma unroll
-      for (int e = 0; e < VKPT; ++e) vreg[e] = *(const bf16x8_t*)(vb + voff[e]);
-    } else {
-      // last, partial tile: rows past the end re-read the last valid row; the mask drops them
-#pragma unroll
-      for (int p = 0; p < KPASS; ++p)
-        kreg[p] = *(const bf16x8_t*)(kb + (uint32_t)min(kr + p * RPP, nrow) * kstride + kc * 8);
-#pragma unroll
-      for (int e = 0; e < VKPT; ++e)
-        vreg[e] = *(const bf16x8_t*)(vb + (uint32_t)min(vgrp * VKPT + e, nrow) * kstride + vc * 8);
+    for (int i = 0; i < INSTS; ++i) {
+      // rows past the end re-read the last valid row; the mask drops them
+      const uint32_t off = lrow[i] <= nrow
+                               ? loff[i]
+                               : (uint32_t)nrow * kstride +
+                                     (uint32_t)(((l % CH) ^ (swz(lrow[i]) % CH)) * 8);
+      char* kdst = (char*)sb.k + (wave * INSTS + i) * 1024;
+      char* vdst = (char*)sb.v + (wave * INSTS + i) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void_t*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + off), (lds_void_t*)vdst, 16, 0, 0);
     }
     if constexpr (GROUP) {
       if (tid < KT) ireg = tid <= nrow ? a.kinfo[ks + tid] : i32x4_t{0x7fffffff, -1, -1, -1};
     }
   };
-
-  if (ntiles > 0) load_tile(kv_lo);
-  for (int it = 0; it < ntiles; ++it) {
-    const int ks = kv_lo + it * KT;
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < KPASS; ++p) *(bf16x8_t*)&sm.k[(kr + p * RPP) * KS + kc * 8] = kreg[p];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (VKPT == 4) {
-        bf16x4_t t4 = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *(bf16x4_t*)&sm.vt[(vc * 8 + e) * VS + vgrp * 4] = t4;
-      } else {
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        bf16x2_t t2 = {vreg[0][e], vreg[1][e]};
-        *(bf16x2_t*)&sm.vt[(vc * 8 + e) * VS + vgrp * 2] = t2;
-      }
-    }
+  auto finish_tile = [&](Smem& sb) {  // this wave's loads have landed; publish key records
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (GROUP) {
       if (tid < KT) {
-        sm.kpos[tid] = ireg[0];
+        sb.kpos[tid] = ireg[0];
 #pragma unroll
-        for (int c = 0; c < NLOW; ++c) sm.klow[c][tid] = ireg[1 + c];
+        for (int c = 0; c < NLOW; ++c) sb.klow[c][tid] = ireg[1 + c];
       }
     }
+  };
+
+  if (ntiles > 0) {
+    issue_tile(kv_lo, smem[0]);
+    finish_tile(smem[0]);
     __syncthreads();
-    if (it + 1 < ntiles) load_tile(ks + KT);
-
-    // ------------------------------------------------------------ tile class for this wave
-    if (!wave_active) continue;
-    const int k_last = ks + KT - 1;
-    int cls;
-    if constexpr (GROUP) {
-      const bool whole = k_last <= kv_hi;
-      const int kp_first = sm.kpos[0];
-      const int kp_last = whole ? sm.kpos[KT - 1] : 0x7fffffff;
-      if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
-      else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
-        cls = NLOW == 0 ? kFull : kFar;
-      else cls = kEdge;
-    } else {
-      if (ks > wq_hi || wq_lo - k_last >= window) cls = kSkip;
-      else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
-      else cls = kEdge;
-    }
-    if (cls == kSkip) continue;
-
-    // ------------------------------------------------------------ S^T = K Q^T
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8_t kf = *(const bf16x8_t*)&sm.k[(kb * 32 + jq) * KS + s * 16 + 8 * hg];
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const int ks = kv_lo + it * KT;
+    Smem& sm = smem[it & 1];
+    if (it + 1 < ntiles) issue_tile(ks + KT, smem[(it + 1) & 1]);  // lands during compute
+    [&] {  // compute on smem[it & 1]; returns early for skipped tiles
+      if (!wave_active) return;
+      const int k_last = ks + KT - 1;
+      int cls;
+      if constexpr (GROUP) {
+        const bool whole = k_last <= kv_hi;
+        const int kp_first = sm.kpos[0];
+        const int kp_last = whole ? sm.kpos[KT - 1] : 0x7fffffff;
+        if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
+        else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
+          cls = NLOW == 0 ? kFull : kFar;
+        else cls = kEdge;
+      } else {
+        if (ks > wq_hi || wq_lo - k_last >= window) cls = kSkip;
+        else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
+        else cls = kEdge;
       }
-    }
+      if (cls == kSkip) return;
 
-    // ------------------------------------------------------------ mask
-    // accumulator element v of tile kb is key kb*32 + 8*(v/4) + 4*hg + v%4 of this tile: four
-    // consecutive keys per group of four elements, read from LDS as one 16-byte vector
-    if (cls != kFull) {
+      // ---------------------------------------------------------- S^T = K Q^T
+      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+      const char* kbase = (const char*)sm.k;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + jq;
+          const int chunk = (2 * s + hg) ^ (swz(row) % CH);
+          bf16x8_t kf = *(const bf16x8_t*)(kbase + row * (2 * DH) + chunk * 16);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+        }
+      }
+
+      // ---------------------------------------------------------- mask
+      // accumulator element v of tile kb is key kb*32 + 8*(v/4) + 4*hg + v%4 of this tile: four
+      // consecutive keys per group of four elements, read from LDS as one 16-byte vector
+      if (cls != kFull) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int kk0 = kb * 32 + 8 * q4 + 4 * hg;
+            bool ok[4] = {true, true, true, true};
+            if constexpr (GROUP) {
+              if (cls == kEdge) {
+                const i32x4_t kp = *(const i32x4_t*)&sm.kpos[kk0];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ok[e] = qpos - kp[e] >= window;
+              }
+#pragma unroll
+              for (int c2 = 0; c2 < NLOW; ++c2) {
+                const i32x4_t kl = *(const i32x4_t*)&sm.klow[c2][kk0];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                  for (int c1 = 0; c1 < NLOW; ++c1) ok[e] = ok[e] && kl[e] != qlow[c1];
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int d = qi - (ks + kk0 + e);
+                ok[e] = d >= 0 && d < window;
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!ok[e]) sacc[kb][4 * q4 + e] = -INFINITY;
+          }
+      }
+
+      // ---------------------------------------------------------- online softmax
+      float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int kk0 = kb * 32 + 8 * q4 + 4 * hg;
-          bool ok[4] = {true, true, true, true};
-          if constexpr (GROUP) {
-            if (cls == kEdge) {
-              const i32x4_t kp = *(const i32x4_t*)&sm.kpos[kk0];
+        for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.sl2;
+      // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
+      // kLazy (log2 units), so p = exp2(x - m_ref) stays below 2^kLazy and O is rescaled on
+      // the first tile and almost never after. lse uses the same reference, so it is exact.
+      constexpr float kLazy = 8.f;
+      const bool bump = tmax > m_run + kLazy;
+      if (__any(bump)) {
+        const float m_next = bump ? tmax : m_run;
+        const float alpha = m_next == -INFINITY ? 1.f : fast_exp2(m_run - m_next);
+        l_run *= alpha;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) ok[e] = qpos - kp[e] >= window;
-            }
-#pragma unroll
-            for (int c2 = 0; c2 < NLOW; ++c2) {
-              const i32x4_t kl = *(const i32x4_t*)&sm.klow[c2][kk0];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int c1 = 0; c1 < NLOW; ++c1) ok[e] = ok[e] && kl[e] != qlow[c1];
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int d = qi - (ks + kk0 + e);
-              ok[e] = d >= 0 && d < window;
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!ok[e]) sacc[kb][4 * q4 + e] = -INFINITY;
-        }
-    }
-
-    // ------------------------------------------------------------ online softmax
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.sl2;
-    // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
-    // kLazy (log2 units), so p = exp2(x - m_ref) stays below 2^kLazy and O is rescaled on
-    // the first tile and almost never after. lse uses the same reference, so it is exact.
-    constexpr float kLazy = 8.f;
-    const bool bump = tmax > m_run + kLazy;
-    if (__any(bump)) {
-      const float m_next = bump ? tmax : m_run;
-      const float alpha = m_next == -INFINITY ? 1.f : fast_exp2(m_run - m_next);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
-      m_run = m_next;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-    bf16x8_t pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int vi = 0; vi < 16; ++vi) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[kb][vi], a.sl2, -m_use));
-        psum += p;
-        pb[kb * 2 + (vi >> 3)][vi & 7] = to_bf16(p);
+        for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+        m_run = m_next;
       }
-    l_run += psum;
-
-    // ------------------------------------------------------------ O^T += V^T P^T
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float psum = 0.f;
+      bf16x8_t pb[4];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int vi = 0; vi < 16; ++vi) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[kb][vi], a.sl2, -m_use));
+          psum += p;
+          pb[kb * 2 + (vi >> 3)][vi & 7] = to_bf16(p);
+        }
+      l_run += psum;
+
+      // ---------------------------------------------------------- O^T += V^T P^T
+      // A operand (32 dims x 16 keys) from row-major V through the transposing LDS read: in
+      // each 16-lane group lane j receives element j%4 of the 8-byte row slice read by lane
+      // 4e + j/4 (e = 0..3). Lane (16g + 4e + m) therefore reads key row base + 8r + 4*hg + e
+      // at dims d*32 + 16*(g%2) + 4m, and receives 4 keys of dim d*32 + lane%32.
+      const char* vbase = (const char*)sm.v;
+      const int e4 = (l & 15) >> 2, m4 = l & 3, g2 = (l >> 4) & 1;
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
-        const int base = (kq >> 1) * 32 + (kq & 1) * 16 + 4 * hg;
-        const __bf16* vp = &sm.vt[(d * 32 + jq) * VS + base];
-        bf16x4_t lo = *(const bf16x4_t*)vp;
-        bf16x4_t hi = *(const bf16x4_t*)(vp + 8);
-        bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kq], oacc[d], 0, 0, 0);
+        const int kbase = (kq >> 1) * 32 + (kq & 1) * 16 + 4 * hg + e4;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {  // consecutive MFMAs feed independent accumulators
+          const int c16 = 4 * d + 2 * g2 + (m4 >> 1);
+          bf16x4_t half[2];
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr) {
+            const int row = kbase + 8 * rr;
+            const char* src = vbase + row * (2 * DH) + ((c16 ^ (swz(row) % CH)) * 16) + (m4 & 1) * 8;
+            typedef short v4i16_t __attribute__((ext_vector_type(4)));
+            v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t*)(lds_void_t*)src);
+            half[rr] = __builtin_bit_cast(bf16x4_t, t);
+          }
+          bf16x8_t vf = {half[0][0], half[0][1], half[0][2], half[0][3],
+                         half[1][0], half[1][1], half[1][2], half[1][3]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kq], oacc[d], 0, 0, 0);
+        }
       }
+    }();
+    if (it + 1 < ntiles) {
+      finish_tile(smem[(it + 1) & 1]);
+      __syncthreads();  // the next tile is in LDS and every wave is done with this one
     }
   }
 
