@@ -7,17 +7,21 @@
 // sees itself), then for each query group g_r the segment members at positions <= p - w'
 // whose lowest group shared with the query is g_r, so every allowed key appears once.
 //
-// The list is cut into `splits` contiguous pieces per (sequence, kv head). A 256-thread block
-// scores one key per thread (G query heads, q in LDS), then accumulates P V with one V row per
-// wave instruction; running (max, sum, O) per head give one partial, and a second kernel merges
-// the partials by their log-sum-exp. The path is HBM-bound: every allowed key costs one K row
-// and one V row of the kv head.
+// The list is cut into `splits` contiguous pieces per (sequence, group of up to 4 query heads
+// of one kv head). A 256-thread block first resolves 256 list entries into key positions in
+// LDS (one per thread, dropping group members owned by a lower shared group), then every
+// 16-lane group takes one key at a time: each lane holds 8 dims of the query heads in
+// registers and reads one coalesced 16-byte chunk of the key's K and V rows, the dot products
+// are reduced across the 16 lanes, and a running (max, sum, O) per head absorbs the key. The
+// 16 lane groups' states are merged through LDS into one partial per block, and a second
+// kernel merges the partials by their log-sum-exp. The path is HBM-bound: every allowed key
+// costs one K row and one V row of the kv head.
 #include "focus_internal.hpp"
 
 namespace focus {
 
-constexpr int kDecChunk = 256;
-constexpr int kDecMaxG = 16;
+constexpr int kDecChunk = 256;   // list entries resolved per pass
+constexpr int kDecHeads = 4;     // query heads per block
 
 int decode_splits(const DecodeShape& s) {
   (void)s;
@@ -35,29 +39,38 @@ struct DecodeArgs {
   const int32_t* cache_idx;
   int B;
   int64_t Lmax;
-  int Hq, Hkv, G, K, top_k, splits;
+  int Hq, Hkv, G, K, top_k, splits, hpb;  // hpb: query heads per block (<= kDecHeads)
   int64_t window;
   float sl2;
-  float* part_o;   // [B, Hkv, splits, G, DH] unnormalised
-  float* part_ml;  // [B, Hkv, splits, G, 2] (running max in log2 units, sum)
+  float* part_o;   // [B, Hq, splits, DH] unnormalised
+  float* part_ml;  // [B, Hq, splits, 2] (running max in log2 units, sum)
 };
+
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {  // sum over the lane's aligned W-lane group
+#pragma unroll
+  for (int o = W / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
 
 template <int DH>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
-  constexpr int VPL = DH / 64;  // value dims per lane in the P V phase
-  __shared__ float qs[kDecMaxG * DH];
-  __shared__ float sc[kDecMaxG * kDecChunk];
-  __shared__ float red[4 * kDecMaxG * DH];
-  __shared__ float stat[kDecMaxG * 2];
-  __shared__ float alpha_s[kDecMaxG];
+  constexpr int CHK = DH / 8;          // 16-byte chunks per row: lanes per key
+  constexpr int KPW = kWave / CHK;     // keys per wave instruction
+  constexpr int NG = 4 * KPW;          // lane groups per block
+  constexpr int HD = kDecHeads;
   __shared__ int kpos[kDecChunk];
+  __shared__ float red_o[NG][HD][DH];
+  __shared__ float red_ml[NG][HD][2];
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int c = l % CHK, grp = wave * KPW + l / CHK;  // chunk of the row, lane group
   const int64_t lin = blockIdx.x;
   const int sp = (int)(lin % a.splits);
-  const int h = (int)((lin / a.splits) % a.Hkv);
-  const int b = (int)(lin / ((int64_t)a.splits * a.Hkv));
-  const int G = a.G;
+  const int hgrp = (int)((lin / a.splits) % (a.Hq / a.hpb));  // head group
+  const int b = (int)(lin / ((int64_t)a.splits * (a.Hq / a.hpb)));
+  const int hq0 = hgrp * a.hpb, h = hq0 / a.G;
+  const int nh = a.hpb;
 
   int64_t L = a.cache_len[b];
   if (L < 1) L = 1;
@@ -94,135 +107,143 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const int64_t v0 = (int64_t)sp * per;
   const int64_t v1 = v0 + per < total ? v0 + per : total;
 
-  for (int i = tid; i < G * DH; i += 256) {
-    int hl = i / DH, d = i % DH;
-    uint16_t bits = a.q[((int64_t)b * a.Hq + h * G + hl) * DH + d];
-    qs[i] = __uint_as_float((uint32_t)bits << 16);
+  // this lane's slice of the query heads, pre-scaled to log2 units
+  float qf[HD][8];
+#pragma unroll
+  for (int hh = 0; hh < HD; ++hh) {
+    const int hq = hq0 + (hh < nh ? hh : 0);
+    const i32x4_t raw = *(const i32x4_t*)(a.q + ((int64_t)b * a.Hq + hq) * DH + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[hh][2 * e] = __uint_as_float((uint32_t)raw[e] << 16) * a.sl2;
+      qf[hh][2 * e + 1] = __uint_as_float((uint32_t)raw[e] & 0xffff0000u) * a.sl2;
+    }
   }
-  if (tid < G) {
-    stat[2 * tid] = -INFINITY;
-    stat[2 * tid + 1] = 0.f;
+  float m_run[HD], l_run[HD], o[HD][8];
+#pragma unroll
+  for (int hh = 0; hh < HD; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
   }
-  float oacc[kDecMaxG][VPL];
-  for (int hl = 0; hl < kDecMaxG; ++hl)
-    for (int e = 0; e < VPL; ++e) oacc[hl][e] = 0.f;
-  __syncthreads();
 
   const int64_t kv_stride = (int64_t)a.Hkv * DH;
-  const uint16_t* kbase = a.kc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH;
-  const uint16_t* vbase = a.vc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH;
+  const uint16_t* kbase = a.kc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
+  const uint16_t* vbase = a.vc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
 
   for (int64_t c0 = v0; c0 < v1; c0 += kDecChunk) {
-    // ---- resolve this thread's key and score it against the G query heads
-    const int64_t vi = c0 + tid;
-    int pos = -1;
-    if (vi < v1) {
-      if (vi < nl) {
-        pos = (int)(lo + vi);
-      } else {
-        int64_t rem = vi - nl;
-        for (int r = 0; r < a.top_k; ++r) {
-          if (rem < cnt[r]) {
-            int cand = cidx[seg_lo[r] + rem];
-            // owned by g_r unless the key also holds a lower query group
-            bool owned = true;
-            const int32_t* kg = a.cache_groups + ((int64_t)b * a.Lmax + cand) * a.top_k;
-            for (int r2 = 0; r2 < a.top_k; ++r2) {
-              int g2 = qg[r2];
-              if (g2 >= 0 && g2 < a.K && g2 < qg[r])
-                for (int r3 = 0; r3 < a.top_k; ++r3) owned = owned && kg[r3] != g2;
+    // ---- resolve list entries c0 + tid into key positions (-1: not this query's key)
+    {
+      const int64_t vi = c0 + tid;
+      int pos = -1;
+      if (vi < v1) {
+        if (vi < nl) {
+          pos = (int)(lo + vi);
+        } else {
+          int64_t rem = vi - nl;
+          for (int r = 0; r < a.top_k; ++r) {
+            if (rem < cnt[r]) {
+              const int cand = cidx[seg_lo[r] + rem];
+              // owned by g_r unless the key also holds a lower query group
+              bool owned = true;
+              const int32_t* kg = a.cache_groups + ((int64_t)b * a.Lmax + cand) * a.top_k;
+              for (int r2 = 0; r2 < a.top_k; ++r2) {
+                const int g2 = qg[r2];
+                if (g2 >= 0 && g2 < a.K && g2 < qg[r])
+                  for (int r3 = 0; r3 < a.top_k; ++r3) owned = owned && kg[r3] != g2;
+              }
+              pos = owned ? cand : -1;
+              break;
             }
-            pos = owned ? cand : -1;
-            break;
+            rem -= cnt[r];
           }
-          rem -= cnt[r];
         }
       }
+      kpos[tid] = pos;
     }
-    kpos[tid] = pos;
-    float s[kDecMaxG];
-    for (int hl = 0; hl < G; ++hl) s[hl] = 0.f;
-    if (pos >= 0) {
-      const uint16_t* kp = kbase + (int64_t)pos * kv_stride;
-      for (int d8 = 0; d8 < DH / 8; ++d8) {
-        i32x4_t raw = *(const i32x4_t*)(kp + d8 * 8);
-        float kf[8];
+    __syncthreads();
+    // ---- lane group grp absorbs entries grp, grp + NG, ... of this chunk, 4 at a time
+    const int nent = (int)(v1 - c0 < kDecChunk ? v1 - c0 : kDecChunk);
+    for (int j0 = grp; j0 < nent; j0 += 4 * NG) {
+      int pk[4];
+      i32x4_t kr[4], vr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * NG;
+        pk[u] = j < nent ? kpos[j] : -1;
+        const int64_t row = pk[u] >= 0 ? pk[u] : 0;
+        kr[u] = *(const i32x4_t*)(kbase + row * kv_stride);
+        vr[u] = *(const i32x4_t*)(vbase + row * kv_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pk[u] < 0) continue;  // uniform within the lane group
+        float kf[8], vf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          uint32_t w = (uint32_t)raw[e];
-          kf[2 * e] = __uint_as_float(w << 16);
-          kf[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+          kf[2 * e] = __uint_as_float((uint32_t)kr[u][e] << 16);
+          kf[2 * e + 1] = __uint_as_float((uint32_t)kr[u][e] & 0xffff0000u);
+          vf[2 * e] = __uint_as_float((uint32_t)vr[u][e] << 16);
+          vf[2 * e + 1] = __uint_as_float((uint32_t)vr[u][e] & 0xffff0000u);
         }
-        for (int hl = 0; hl < G; ++hl) {
-          const float* qq = qs + hl * DH + d8 * 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[hl] += qq[e] * kf[e];
+        for (int hh = 0; hh < HD; ++hh) {
+          if (hh >= nh) break;
+          float sdot = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(qf[hh][e], kf[e], sdot);
+          sdot = group_sum<CHK>(sdot);
+          // lazy running max: rescale only when the score passes the reference by 2^8
+          if (sdot > m_run[hh] + 8.f) {
+            const float alpha = m_run[hh] == -INFINITY ? 0.f : fast_exp2(m_run[hh] - sdot);
+            l_run[hh] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
+            m_run[hh] = sdot;
+          }
+          const float pw = fast_exp2(sdot - m_run[hh]);
+          l_run[hh] += pw;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pw, vf[e], o[hh][e]);
         }
       }
     }
-    for (int hl = 0; hl < G; ++hl) sc[hl * kDecChunk + tid] = pos >= 0 ? s[hl] * a.sl2 : -INFINITY;
-    __syncthreads();
-    // ---- online softmax statistics per head: wave w handles heads w, w+4, ...
-    for (int hl = wave; hl < G; hl += 4) {
-      float mx = -INFINITY;
-      for (int i = l; i < kDecChunk; i += 64) mx = fmaxf(mx, sc[hl * kDecChunk + i]);
-      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
-      const float m_old = stat[2 * hl];
-      const float m_new = fmaxf(m_old, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      float sum = 0.f;
-      for (int i = l; i < kDecChunk; i += 64) {
-        float pp = fast_exp2(sc[hl * kDecChunk + i] - m_use);
-        sc[hl * kDecChunk + i] = pp;
-        sum += pp;
-      }
-      for (int o = 32; o >= 1; o >>= 1) sum += shfl_xor_f(sum, o);
-      if (l == 0) {
-        const float alpha = fast_exp2(m_old - m_use);
-        stat[2 * hl] = m_new;
-        stat[2 * hl + 1] = stat[2 * hl + 1] * alpha + sum;
-        alpha_s[hl] = alpha;
-      }
-    }
-    __syncthreads();
-    // ---- rescale O and accumulate P V: wave w takes keys w, w+4, ...; lane l dims VPL*l..
-    for (int hl = 0; hl < G; ++hl) {
-      const float alpha = alpha_s[hl];
-      for (int e = 0; e < VPL; ++e) oacc[hl][e] *= alpha;
-    }
-    for (int kk = wave; kk < kDecChunk; kk += 4) {
-      const int kp = kpos[kk];
-      if (kp < 0) continue;
-      float vf[VPL];
-      if constexpr (VPL == 2) {
-        uint32_t w = *(const uint32_t*)(vbase + (int64_t)kp * kv_stride + 2 * l);
-        vf[0] = __uint_as_float(w << 16);
-        vf[1] = __uint_as_float(w & 0xffff0000u);
-      } else {
-        uint16_t w = vbase[(int64_t)kp * kv_stride + l];
-        vf[0] = __uint_as_float((uint32_t)w << 16);
-      }
-      for (int hl = 0; hl < G; ++hl) {
-        const float pp = sc[hl * kDecChunk + kk];
-        for (int e = 0; e < VPL; ++e) oacc[hl][e] += pp * vf[e];
-      }
-    }
     __syncthreads();
   }
-  // ---- reduce the 4 waves' O and write the partial
-  for (int hl = 0; hl < G; ++hl)
-    for (int e = 0; e < VPL; ++e) red[(wave * kDecMaxG + hl) * DH + VPL * l + e] = oacc[hl][e];
+
+  // ---- merge the lane groups' states and write this block's partial per head
+  if (c == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HD; ++hh) {
+      red_ml[grp][hh][0] = m_run[hh];
+      red_ml[grp][hh][1] = l_run[hh];
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < HD; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_o[grp][hh][c * 8 + e] = o[hh][e];
   __syncthreads();
-  const int64_t pbase = (((int64_t)b * a.Hkv + h) * a.splits + sp) * G;
-  for (int i = tid; i < G * DH; i += 256) {
-    int hl = i / DH, d = i % DH;
-    float x = 0.f;
-    for (int w = 0; w < 4; ++w) x += red[(w * kDecMaxG + hl) * DH + d];
-    a.part_o[(pbase + hl) * DH + d] = x;
-  }
-  if (tid < G) {
-    a.part_ml[(pbase + tid) * 2] = stat[2 * tid];
-    a.part_ml[(pbase + tid) * 2 + 1] = stat[2 * tid + 1];
+  for (int i = tid; i < nh * DH; i += 256) {
+    const int hh = i / DH, d = i % DH;
+    float M = -INFINITY;
+    for (int g = 0; g < NG; ++g) M = fmaxf(M, red_ml[g][hh][0]);
+    float lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY)
+      for (int g = 0; g < NG; ++g) {
+        const float m = red_ml[g][hh][0];
+        if (m == -INFINITY) continue;
+        const float w = fast_exp2(m - M);
+        lsum += w * red_ml[g][hh][1];
+        acc += w * red_o[g][hh][d];
+      }
+    const int64_t pi = ((int64_t)b * a.Hq + hq0 + hh) * a.splits + sp;
+    a.part_o[pi * DH + d] = acc;
+    if (d == 0) {
+      a.part_ml[pi * 2] = M;
+      a.part_ml[pi * 2 + 1] = lsum;
+    }
   }
 }
 
@@ -233,18 +254,16 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(const float* __restr
                                                             uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;  // b * Hq + hq
-  const int b = (int)(bh / Hq), hq = (int)(bh % Hq);
-  const int h = hq / G, hl = hq % G;
+  (void)Hq;
+  (void)Hkv;
+  (void)G;
   const int d = threadIdx.x;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
-    int64_t pi = (((int64_t)b * Hkv + h) * splits + s) * G + hl;
-    M = fmaxf(M, part_ml[pi * 2]);
-  }
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(bh * splits + s) * 2]);
   float den = 0.f, acc = 0.f;
   if (M != -INFINITY) {
     for (int s = 0; s < splits; ++s) {
-      int64_t pi = (((int64_t)b * Hkv + h) * splits + s) * G + hl;
+      int64_t pi = bh * splits + s;
       float m = part_ml[pi * 2];
       if (m == -INFINITY) continue;
       float w = fast_exp2(m - M);
@@ -284,7 +303,8 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   a.sl2 = s.scale * kLog2e;
   a.part_o = part_o;
   a.part_ml = part_ml;
-  const int64_t blocks = (int64_t)s.B * s.Hkv * s.splits;
+  a.hpb = s.G < kDecHeads ? s.G : kDecHeads;
+  const int64_t blocks = (int64_t)s.B * (s.Hq / a.hpb) * s.splits;
   if (s.dh == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
