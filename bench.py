@@ -41,6 +41,48 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ------------------------------------------------------------------ measured HBM traffic
+KERNEL_SRC = os.path.join(ROOT, "learned_centroid_gated_amd", "csrc", "attention_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "group_attention_gqa70b_n128k_traffic.md")
+CALIBRATION_BYTES = 1 << 30  # one fp32 negation over 2^28 elements reads and writes 1 GiB each
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the group-attention kernel, from the FETCH_SIZE/WRITE_SIZE
+    counter runs summarised in profiles/ (scaled by the same counters on a plain copy of
+    known size); None when the summary is absent or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != source_sha256(KERNEL_SRC):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibration_copy():
+    """One fp32 negation of 2^28 elements (1 GiB read, 1 GiB written): the known-size kernel
+    whose FETCH_SIZE/WRITE_SIZE counters scale the counters of the Focus kernels."""
+    x = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+
+
 # ------------------------------------------------------------------ HIP events (ctypes)
 class Hip:
     def __init__(self):
@@ -190,7 +232,9 @@ def prefill_bench(c, steps, warmup, hip):
         p = gpairs if dom == "group_attention" else wpairs
         ach = flops_pair * p / (stage_ms[dom] * 1e-3) / 1e12
         res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic() if (dom == "group_attention" and
+                                                            c.name == "gqa70b_n128k") else None,
                            "algorithmic_per_launch": flops_pair * p, "avg_launch_ms": stage_ms[dom]}
     else:
         ach = gather_bytes / (stage_ms[dom] * 1e-3) / 1e9
@@ -341,6 +385,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB copy, to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the Focus path here runs on a single MI355X and has no "
@@ -349,6 +395,8 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = Hip()
+    if args.calibrate_copy:
+        calibration_copy()
     cfg = {x.name: x for x in CONFIGS}
     c3 = cfg["gqa70b_n128k"]
     res3, st3 = prefill_bench(c3, args.steps, args.warmup, hip)
