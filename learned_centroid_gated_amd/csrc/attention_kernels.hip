@@ -18,6 +18,9 @@
 // lane pair (l, l^32) and need a single cross-lane exchange. O^T = V^T P^T reuses the S^T
 // accumulator layout directly as the B operand; V is stored transposed in LDS so the A
 // operand (32 dims x 16 keys) is two 8-byte reads per lane.
+#include <cstddef>
+#include <type_traits>
+
 #include "focus_internal.hpp"
 
 namespace focus {
@@ -157,14 +160,21 @@ constexpr int KT = 64;  // keys per kv tile
 // even parts differ across any 4 consecutive rows, so both access patterns are free of bank
 // conflicts: 16 lanes reading one chunk of 16 consecutive rows (K as the MFMA A operand) and
 // 16 lanes reading 2 adjacent chunks of 4 consecutive rows (V through the transposing read).
+// swz depends on the low 4 bits of the row only, so rows 16 apart share a permutation and every
+// lane's LDS addresses differ between tiles and row blocks by compile-time constants.
 __device__ __forceinline__ int swz(int row) {
   return ((row & 3) << 1) | (((row >> 2) & 1) << 3) | ((row >> 3) & 1);
 }
 
-template <int DH>
+// Ownership bias rows (group pass, MKS > 0): mrow[j][key][t] is bf16 1.0 when the key shares a
+// lower group with query token 16 j + t of the tile, else 0. One extra MFMA k-step per 16
+// tokens multiplies them with a per-lane one-hot of the row's token scaled by -2^100, which
+// pushes every excluded score to about -2^100 before the softmax sees it.
+template <int DH, int MKS>
 struct FlashSmem {
   __bf16 k[KT * DH];
   __bf16 v[KT * DH];
+  __bf16 mrow[MKS > 0 ? MKS : 1][KT][16];
   int kpos[KT];
   int klow[3][KT];
 };
@@ -173,19 +183,46 @@ struct FlashSmem {
 enum { kSkip = 0, kEdge = 1, kFar = 2, kFull = 3 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// One wave-wide global_load_lds_dwordx4: lane L copies 16 bytes from base + voff (base uniform,
+// voff per lane) to LDS byte lds_dst + 16 L. Issued through inline asm so the compiler does not
+// treat the copy as a pending write to every LDS location: with the builtin it waits for the
+// whole copy before the first LDS read that follows, which serialises the prefetch of the next
+// tile with the compute on the current one. The caller waits (vmcnt) before the data is read.
+// The LDS destination goes in as a pointer operand (not an integer), so the compiler keeps
+// treating the buffer as written by the asm statement.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, void* lds_dst) {
+  lds_char_t* m = (lds_char_t*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory");
+}
+
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+constexpr float kMaskBias = -0x1p100f;   // ownership bias of an excluded pair (before scaling)
+constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully masked rows
 
 // NLOW = top_k - 1 lower groups per membership matter for the ownership rule (group pass).
-template <int DH, bool GROUP, int NLOW>
+// MKS = 16-token k-steps of the MFMA ownership bias (0: per-element compare instead).
+template <int DH, bool GROUP, int NLOW, int MKS>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
-  using Smem = FlashSmem<DH>;
+  using Smem = FlashSmem<DH, MKS>;
   constexpr int CH = DH / 8;             // 16-byte chunks per key row
   constexpr int ROWS_PER_INST = 64 / CH; // key rows one wave-wide 1 KB LDS load covers
   constexpr int INSTS = KT / ROWS_PER_INST / 4;  // per wave, for each of K and V
   constexpr int NS = DH / 16;            // MFMA k-steps over the head dimension
   constexpr int ND = DH / 32;            // 32-wide output tiles over the head dimension
+  constexpr int RB = 2 * DH;             // bytes per key row
+  static_assert(MKS == 0 || (GROUP && NLOW > 0), "ownership bias only in the group pass");
   __shared__ __attribute__((aligned(1024))) Smem smem[2];  // double buffer: one barrier per tile
+  __shared__ __attribute__((aligned(16))) int qlow_s[3][32];  // MKS > 0: query tokens' lower groups, -2 if none
 
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, jq = l & 31, hg = l >> 5;
+  const int tid = threadIdx.x, l = tid & 63, jq = l & 31, hg = l >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------------------------------------------------------- work item
   const int W = GROUP ? a.tile_pre[a.K] : a.tiles_per_head;
@@ -255,6 +292,23 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       qreg[s] = qvalid ? *(const bf16x8_t*)(qp + 16 * s) : bf16x8_t{};
   }
 
+  // query side of the ownership bias: -2^100 at this row's token (T <= 32: token = jq % T)
+  bf16x8_t qm[MKS > 0 ? MKS : 1];
+  if constexpr (MKS > 0) {
+    const int tw = jq % a.T;
+#pragma unroll
+    for (int j = 0; j < MKS; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qm[j][e] = (__bf16)(16 * j + 8 * hg + e == tw ? kMaskBias : 0.f);
+    if (tid < 32) {
+      const int t = tid, qt = q0 + t;
+      i32x4_t info = {0, -2, -2, -2};
+      if (t < a.T && qt < q1) info = a.kinfo[qt];
+#pragma unroll
+      for (int c = 0; c < NLOW; ++c) qlow_s[c][t] = (t < a.T && qt < q1 && info[1 + c] >= 0) ? info[1 + c] : -2;
+    }
+  }
+
   // ---------------------------------------------------------------- kv tile range
   int ntiles;
   if constexpr (GROUP) {
@@ -275,46 +329,128 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // ---------------------------------------------------------------- per-lane LDS addresses
+  // Byte offsets from smem[0]; the buffer parity, the row block (32 keys for K, 16 for V) and
+  // the mask k-step are added as instruction immediates.
+  const char* lds = (const char*)smem;
+  uint32_t krd[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    krd[s] = (uint32_t)(jq * RB + (((2 * s + hg) ^ (swz(jq) % CH)) * 16));
+  // V through the transposing read: in each 16-lane group lane j receives element j%4 of the
+  // 8-byte row slice read by lane 4e + j/4 (e = 0..3). Lane (16g + 4e + m) reads key row
+  // 16 kq + 8 rr + 4 hg + e at dims 32 d + 16 (g%2) + 4m and so receives 4 keys of dim
+  // 32 d + lane%32.
+  const int e4 = (l & 15) >> 2, m4 = l & 3, g2 = (l >> 4) & 1;
+  uint32_t vrd[ND][2];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = 4 * hg + e4 + 8 * rr;
+      const int c16 = 4 * d + 2 * g2 + (m4 >> 1);
+      vrd[d][rr] = (uint32_t)(offsetof(Smem, v) + row * RB + ((c16 ^ (swz(row) % CH)) * 16) +
+                              (m4 & 1) * 8);
+    }
+  const uint32_t mrd = (uint32_t)(offsetof(Smem, mrow) + jq * 32 + hg * 16);
+
   // ---------------------------------------------------------------- tile loads
   // Wave w moves key rows [w*KT/4, (w+1)*KT/4) of K and of V straight into LDS with
   // global_load_lds_dwordx4: one instruction fills 1 KB of LDS, lane L landing at byte 16*L,
   // i.e. row L / CH of the instruction's block, swizzled position L % CH, so lane L fetches the
-  // global chunk (L % CH) ^ swz(row).
-  const uint32_t kstride = (uint32_t)a.Hkv * DH;  // elements between consecutive key rows
-  const uint16_t* khead = a.k + (int64_t)h * DH;
-  const uint16_t* vhead = a.v + (int64_t)h * DH;
+  // global chunk (L % CH) ^ swz(row). Per-lane byte offsets are fixed; the tile moves a uniform
+  // base.
+  const uint32_t kstride_b = (uint32_t)a.Hkv * RB;  // bytes between consecutive key rows
+  const char* khead = (const char*)a.k + (int64_t)h * RB;
+  const char* vhead = (const char*)a.v + (int64_t)h * RB;
+  uint32_t gofs[INSTS], gchunk[INSTS];
   int lrow[INSTS];
-  uint32_t loff[INSTS];
 #pragma unroll
   for (int i = 0; i < INSTS; ++i) {
     lrow[i] = (wave * INSTS + i) * ROWS_PER_INST + l / CH;
-    loff[i] = (uint32_t)lrow[i] * kstride + (uint32_t)(((l % CH) ^ (swz(lrow[i]) % CH)) * 8);
+    gchunk[i] = (uint32_t)(((l % CH) ^ (swz(lrow[i]) % CH)) * 16);
+    gofs[i] = (uint32_t)lrow[i] * kstride_b + gchunk[i];
   }
   i32x4_t ireg = {0x7fffffff, -1, -1, -1};
+  const int kkey = MKS > 0 ? (tid >> 2) : tid;  // key whose record this thread loads
 
-  auto issue_tile = [&](int ks, Smem& sb) {
-    const uint16_t* kb = khead + (int64_t)ks * kstride;  // uniform tile base
-    const uint16_t* vb = vhead + (int64_t)ks * kstride;
+  auto issue_tile = [&](int ks, Smem& sb) __attribute__((always_inline)) {
+    const char* kb = khead + (int64_t)ks * kstride_b;  // uniform tile base
+    const char* vb = vhead + (int64_t)ks * kstride_b;
     const int nrow = kv_hi - ks;  // rows 0..nrow of the tile are valid
+    if (nrow >= KT - 1) {
 #pragma unroll
-    for (int i = 0; i < INSTS; ++i) {
+      for (int i = 0; i < INSTS; ++i) {
+        dma16(kb, gofs[i], (char*)sb.k + (wave * INSTS + i) * 1024);
+        dma16(vb, gofs[i], (char*)sb.v + (wave * INSTS + i) * 1024);
+      }
+    } else {
       // rows past the end re-read the last valid row; the mask drops them
-      const uint32_t off = lrow[i] <= nrow
-                               ? loff[i]
-                               : (uint32_t)nrow * kstride +
-                                     (uint32_t)(((l % CH) ^ (swz(lrow[i]) % CH)) * 8);
-      char* kdst = (char*)sb.k + (wave * INSTS + i) * 1024;
-      char* vdst = (char*)sb.v + (wave * INSTS + i) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void_t*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + off), (lds_void_t*)vdst, 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < INSTS; ++i) {
+        const uint32_t off = lrow[i] <= nrow ? gofs[i] : (uint32_t)nrow * kstride_b + gchunk[i];
+        dma16(kb, off, (char*)sb.k + (wave * INSTS + i) * 1024);
+        dma16(vb, off, (char*)sb.v + (wave * INSTS + i) * 1024);
+      }
     }
     if constexpr (GROUP) {
-      if (tid < KT) ireg = tid <= nrow ? a.kinfo[ks + tid] : i32x4_t{0x7fffffff, -1, -1, -1};
+      // load only the record fields in use: a partly dead load destination would make the
+      // compiler wait for this load wherever it reuses those registers
+      if (kkey < KT) {
+        const int* rec = (const int*)&a.kinfo[ks + kkey];
+        if constexpr (NLOW == 0) {
+          ireg[0] = kkey <= nrow ? rec[0] : 0x7fffffff;
+        } else if constexpr (NLOW == 1) {
+          const i32x2_t t = kkey <= nrow ? *(const i32x2_t*)rec : i32x2_t{0x7fffffff, -1};
+          ireg[0] = t[0];
+          ireg[1] = t[1];
+        } else if constexpr (NLOW == 2) {
+          const bool in = kkey <= nrow;
+          ireg[0] = in ? rec[0] : 0x7fffffff;
+          ireg[1] = in ? rec[1] : -1;
+          ireg[2] = in ? rec[2] : -1;
+        } else {
+          ireg = kkey <= nrow ? *(const i32x4_t*)rec : i32x4_t{0x7fffffff, -1, -1, -1};
+        }
+      }
     }
   };
-  auto finish_tile = [&](Smem& sb) {  // this wave's loads have landed; publish key records
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (GROUP) {
+  // Waits for this wave's loads go through the builtin (not inline asm), so the compiler's own
+  // wait tracking sees them. They are placed on every path into the tile loop and at the end of
+  // every step, so no load can look outstanding at the loop head: the compiler would otherwise
+  // wait for the prefetch of the next tile before computing on the current one.
+  auto finish_tile = [&](Smem& sb) __attribute__((always_inline)) {  // loads landed: publish
+    if constexpr (GROUP && MKS > 0) {
+      // thread (key, quarter tq) writes the bias row entries of tokens [tq*TPT, (tq+1)*TPT)
+      constexpr int TPT = MKS * 4;
+      const int tq = tid & 3;
+      if (tq == 0) sb.kpos[kkey] = ireg[0];
+      uint32_t word[TPT / 2];
+#pragma unroll
+      for (int u2 = 0; u2 < TPT / 2; ++u2) word[u2] = 0;
+#pragma unroll
+      for (int c1 = 0; c1 < NLOW; ++c1) {
+#pragma unroll
+        for (int u4 = 0; u4 < TPT / 4; ++u4) {
+          const i32x4_t ql = *(const i32x4_t*)&qlow_s[c1][tq * TPT + 4 * u4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bool hit = false;
+#pragma unroll
+            for (int c2 = 0; c2 < NLOW; ++c2) hit = hit || ql[e] == ireg[1 + c2];
+            const int u = 4 * u4 + e;
+            word[u >> 1] |= hit ? (0x3F80u << (16 * (u & 1))) : 0u;
+          }
+        }
+      }
+      const int t0 = tq * TPT;
+      char* dst = (char*)&sb.mrow[t0 >> 4][kkey][t0 & 15];
+      if constexpr (TPT == 4) {
+        *(i32x2_t*)dst = i32x2_t{(int)word[0], (int)word[1]};
+      } else {
+        *(i32x4_t*)dst = i32x4_t{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
+      }
+    } else if constexpr (GROUP) {
       if (tid < KT) {
         sb.kpos[tid] = ireg[0];
 #pragma unroll
@@ -323,64 +459,63 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    issue_tile(kv_lo, smem[0]);
-    finish_tile(smem[0]);
-    __syncthreads();
-  }
-  for (int it = 0; it < ntiles; ++it) {
-    const int ks = kv_lo + it * KT;
-    Smem& sm = smem[it & 1];
-    if (it + 1 < ntiles) issue_tile(ks + KT, smem[(it + 1) & 1]);  // lands during compute
-    [&] {  // compute on smem[it & 1]; returns early for skipped tiles
-      if (!wave_active) return;
-      const int k_last = ks + KT - 1;
-      int cls;
-      if constexpr (GROUP) {
-        const bool whole = k_last <= kv_hi;
-        const int kp_first = sm.kpos[0];
-        const int kp_last = whole ? sm.kpos[KT - 1] : 0x7fffffff;
-        if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
-        else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
-          cls = NLOW == 0 ? kFull : kFar;
-        else cls = kEdge;
-      } else {
-        if (ks > wq_hi || wq_lo - k_last >= window) cls = kSkip;
-        else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
-        else cls = kEdge;
-      }
-      if (cls == kSkip) return;
+  // ---------------------------------------------------------------- one kv tile
+  auto compute_tile = [&](int ks, const Smem& sm, const uint32_t par) __attribute__((always_inline)) {
+    if (!wave_active) return;
+    const int k_last = ks + KT - 1;
+    int cls;
+    if constexpr (GROUP) {
+      const bool whole = k_last <= kv_hi;
+      const int kp_first = __builtin_amdgcn_readfirstlane(sm.kpos[0]);
+      const int kp_last = whole ? __builtin_amdgcn_readfirstlane(sm.kpos[KT - 1]) : 0x7fffffff;
+      if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
+      else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
+        cls = (NLOW == 0 || MKS > 0) ? kFull : kFar;
+      else cls = kEdge;
+    } else {
+      if (ks > wq_hi || wq_lo - k_last >= window) cls = kSkip;
+      else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
+      else cls = kEdge;
+    }
+    if (cls == kSkip) return;
 
-      // ---------------------------------------------------------- S^T = K Q^T
-      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-      const char* kbase = (const char*)sm.k;
+    // ------------------------------------------------------------ S^T = K Q^T (+ bias)
+    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+    if constexpr (MKS > 0) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int j = 0; j < MKS; ++j)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + jq;
-          const int chunk = (2 * s + hg) ^ (swz(row) % CH);
-          bf16x8_t kf = *(const bf16x8_t*)(kbase + row * (2 * DH) + chunk * 16);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+          const bf16x8_t mf = *(const bf16x8_t*)(lds + mrd + par + (j * KT + kb * 32) * 32);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, qm[j], sacc[kb], 0, 0, 0);
         }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t kf = *(const bf16x8_t*)(lds + krd[s] + par + kb * 32 * RB);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
       }
+    }
 
-      // ---------------------------------------------------------- mask
-      // accumulator element v of tile kb is key kb*32 + 8*(v/4) + 4*hg + v%4 of this tile: four
-      // consecutive keys per group of four elements, read from LDS as one 16-byte vector
-      if (cls != kFull) {
+    // ------------------------------------------------------------ mask
+    // accumulator element v of tile kb is key kb*32 + 8*(v/4) + 4*hg + v%4 of this tile: four
+    // consecutive keys per group of four elements, read from LDS as one 16-byte vector
+    if (cls != kFull) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int kk0 = kb * 32 + 8 * q4 + 4 * hg;
-            bool ok[4] = {true, true, true, true};
-            if constexpr (GROUP) {
-              if (cls == kEdge) {
-                const i32x4_t kp = *(const i32x4_t*)&sm.kpos[kk0];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kk0 = kb * 32 + 8 * q4 + 4 * hg;
+          bool ok[4] = {true, true, true, true};
+          if constexpr (GROUP) {
+            if (cls == kEdge) {
+              const i32x4_t kp = *(const i32x4_t*)&sm.kpos[kk0];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ok[e] = qpos - kp[e] >= window;
-              }
+              for (int e = 0; e < 4; ++e) ok[e] = qpos - kp[e] >= window;
+            }
+            if constexpr (MKS == 0) {
 #pragma unroll
               for (int c2 = 0; c2 < NLOW; ++c2) {
                 const i32x4_t kl = *(const i32x4_t*)&sm.klow[c2][kk0];
@@ -389,85 +524,100 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 #pragma unroll
                   for (int c1 = 0; c1 < NLOW; ++c1) ok[e] = ok[e] && kl[e] != qlow[c1];
               }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int d = qi - (ks + kk0 + e);
-                ok[e] = d >= 0 && d < window;
-              }
             }
+          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!ok[e]) sacc[kb][4 * q4 + e] = -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+              const int d = qi - (ks + kk0 + e);
+              ok[e] = d >= 0 && d < window;
+            }
           }
-      }
-
-      // ---------------------------------------------------------- online softmax
-      float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.sl2;
-      // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
-      // kLazy (log2 units), so p = exp2(x - m_ref) stays below 2^kLazy and O is rescaled on
-      // the first tile and almost never after. lse uses the same reference, so it is exact.
-      constexpr float kLazy = 8.f;
-      const bool bump = tmax > m_run + kLazy;
-      if (__any(bump)) {
-        const float m_next = bump ? tmax : m_run;
-        const float alpha = m_next == -INFINITY ? 1.f : fast_exp2(m_run - m_next);
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
-        m_run = m_next;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-      bf16x8_t pb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int vi = 0; vi < 16; ++vi) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[kb][vi], a.sl2, -m_use));
-          psum += p;
-          pb[kb * 2 + (vi >> 3)][vi & 7] = to_bf16(p);
+          for (int e = 0; e < 4; ++e)
+            if (!ok[e]) sacc[kb][4 * q4 + e] = -INFINITY;
         }
-      l_run += psum;
+    }
 
-      // ---------------------------------------------------------- O^T += V^T P^T
-      // A operand (32 dims x 16 keys) from row-major V through the transposing LDS read: in
-      // each 16-lane group lane j receives element j%4 of the 8-byte row slice read by lane
-      // 4e + j/4 (e = 0..3). Lane (16g + 4e + m) therefore reads key row base + 8r + 4*hg + e
-      // at dims d*32 + 16*(g%2) + 4m, and receives 4 keys of dim d*32 + lane%32.
-      const char* vbase = (const char*)sm.v;
-      const int e4 = (l & 15) >> 2, m4 = l & 3, g2 = (l >> 4) & 1;
+    // ------------------------------------------------------------ online softmax
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const int kbase = (kq >> 1) * 32 + (kq & 1) * 16 + 4 * hg + e4;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {  // consecutive MFMAs feed independent accumulators
-          const int c16 = 4 * d + 2 * g2 + (m4 >> 1);
-          bf16x4_t half[2];
+      for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    if constexpr (MKS > 0) tmax = tmax < kMaskFloor ? -INFINITY : tmax;
+    tmax *= a.sl2;
+    // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
+    // kLazy (log2 units), so p = exp2(x - m_ref) stays below 2^kLazy and O is rescaled on
+    // the first tile and almost never after. lse uses the same reference, so it is exact.
+    constexpr float kLazy = 8.f;
+    const bool bump = tmax > m_run + kLazy;
+    if (__any(bump)) {
+      const float m_next = bump ? tmax : m_run;
+      const float alpha = m_next == -INFINITY ? 1.f : fast_exp2(m_run - m_next);
+      l_run *= alpha;
 #pragma unroll
-          for (int rr = 0; rr < 2; ++rr) {
-            const int row = kbase + 8 * rr;
-            const char* src = vbase + row * (2 * DH) + ((c16 ^ (swz(row) % CH)) * 16) + (m4 & 1) * 8;
-            typedef short v4i16_t __attribute__((ext_vector_type(4)));
-            v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16_t*)(lds_void_t*)src);
-            half[rr] = __builtin_bit_cast(bf16x4_t, t);
-          }
-          bf16x8_t vf = {half[0][0], half[0][1], half[0][2], half[0][3],
-                         half[1][0], half[1][1], half[1][2], half[1][3]};
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kq], oacc[d], 0, 0, 0);
-        }
+      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+      m_run = m_next;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int vi = 0; vi < 16; ++vi) {
+        const float p = fast_exp2(__builtin_fmaf(sacc[kb][vi], a.sl2, -m_use));
+        psum[vi & 3] += p;
+        pb[kb * 2 + (vi >> 3)][vi & 7] = to_bf16(p);
       }
-    }();
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+
+    // ------------------------------------------------------------ O^T += V^T P^T
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const uint32_t kqo = ((kq >> 1) * 32 + (kq & 1) * 16) * RB;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {  // consecutive MFMAs feed independent accumulators
+        bf16x4_t half[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          typedef short v4i16_t __attribute__((ext_vector_type(4)));
+          const char* src = lds + vrd[d][rr] + par + kqo;
+          v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(lds_void_t*)src);
+          half[rr] = __builtin_bit_cast(bf16x4_t, t);
+        }
+        bf16x8_t vf = {half[0][0], half[0][1], half[0][2], half[0][3],
+                       half[1][0], half[1][1], half[1][2], half[1][3]};
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kq], oacc[d], 0, 0, 0);
+      }
+    }
+  };
+
+  if constexpr (MKS > 0) __syncthreads();  // qlow_s is read by every tile's bias rows
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // query rows and records are in registers
+  if (ntiles > 0) {
+    issue_tile(kv_lo, smem[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    finish_tile(smem[0]);
+    __syncthreads();
+  }
+  // unrolled by two so each copy addresses one LDS buffer through immediates
+  auto step = [&](int it, auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    const int ks = kv_lo + it * KT;
+    if (it + 1 < ntiles) issue_tile(ks + KT, smem[P ^ 1]);  // lands during compute
+    compute_tile(ks, smem[P], (uint32_t)(P * sizeof(Smem)));
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (it + 1 < ntiles) {
-      finish_tile(smem[(it + 1) & 1]);
+      finish_tile(smem[P ^ 1]);
       __syncthreads();  // the next tile is in LDS and every wave is done with this one
     }
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -543,12 +693,20 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
 }
 
-template <bool GROUP, int NLOW>
+template <bool GROUP, int NLOW, int MKS>
 static void flash_dispatch_dh(const FlashArgs& fa, int dh, int64_t blocks, hipStream_t stream) {
   if (dh == 128)
-    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW>), dim3(blocks), dim3(256), 0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS>), dim3(blocks), dim3(256), 0, stream, fa);
   else
-    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW>), dim3(blocks), dim3(256), 0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS>), dim3(blocks), dim3(256), 0, stream, fa);
+}
+
+template <int NLOW>
+static void flash_dispatch_group(const FlashArgs& fa, int dh, int mks, int64_t blocks,
+                                 hipStream_t stream) {
+  if (mks == 1) flash_dispatch_dh<true, NLOW, 1>(fa, dh, blocks, stream);
+  else if (mks == 2) flash_dispatch_dh<true, NLOW, 2>(fa, dh, blocks, stream);
+  else flash_dispatch_dh<true, NLOW, 0>(fa, dh, blocks, stream);
 }
 
 hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
@@ -577,11 +735,14 @@ hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const u
   const int64_t w_max = (s.nk + fa.T - 1) / fa.T + s.K;
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * w_max);
   if (blocks <= 0) return hipSuccess;
+  // The ownership rule runs as an MFMA bias when a wave's rows span at most 32 tokens and the
+  // scaled bias (-2^100 * scale * log2 e) still drives exp2 to zero; else per-element compares.
+  const int mks = (fa.T <= 32 && fa.sl2 >= 0x1p-60f) ? (fa.T <= 16 ? 1 : 2) : 0;
   switch (s.top_k) {
-    case 1: flash_dispatch_dh<true, 0>(fa, s.dh, blocks, stream); break;
-    case 2: flash_dispatch_dh<true, 1>(fa, s.dh, blocks, stream); break;
-    case 3: flash_dispatch_dh<true, 2>(fa, s.dh, blocks, stream); break;
-    default: flash_dispatch_dh<true, 3>(fa, s.dh, blocks, stream); break;
+    case 1: flash_dispatch_dh<true, 0, 0>(fa, s.dh, blocks, stream); break;
+    case 2: flash_dispatch_group<1>(fa, s.dh, mks, blocks, stream); break;
+    case 3: flash_dispatch_group<2>(fa, s.dh, mks, blocks, stream); break;
+    default: flash_dispatch_group<3>(fa, s.dh, mks, blocks, stream); break;
   }
   return hipGetLastError();
 }
@@ -610,7 +771,7 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
   if (blocks <= 0) return hipSuccess;
-  flash_dispatch_dh<false, 0>(fa, s.dh, blocks, stream);
+  flash_dispatch_dh<false, 0, 0>(fa, s.dh, blocks, stream);
   return hipGetLastError();
 }
 
