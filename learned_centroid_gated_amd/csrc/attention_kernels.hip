@@ -163,7 +163,7 @@ constexpr int KT = 64;  // keys per kv tile
 // swz depends on the low 4 bits of the row only, so rows 16 apart share a permutation and every
 // lane's LDS addresses differ between tiles and row blocks by compile-time constants.
 __device__ __forceinline__ int swz(int row) {
-  return ((row & 3) << 1) | (((row >> 2) & 1) << 3) | ((row >> 3) & 1);
+  return ((row & 1) << 3) | (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
 }
 
 // Ownership bias rows (group pass, MKS > 0): mrow[j][key][t] is bf16 1.0 when the key shares a
