@@ -1,5 +1,6 @@
-// Centroid group assignment on gfx950: scores S = (H W_g) C^T on fp32 MFMA, log-domain
-// Sinkhorn balancing and top-k membership.
+// Centroid group assignment on gfx950: scores S = (H W_g) C^T on the bf16 matrix cores (fp32
+// operands split exactly into three bf16 parts), log-domain Sinkhorn balancing and top-k
+// membership.
 //
 // Method: "Why Attend to Everything? Focus is the Key" (Chinese technical summary,
 // gist.science/zh, section 2.1.1: projection into centroid space, similarity to K centroids,
@@ -9,20 +10,46 @@
 
 namespace focus {
 
-// ============================================================================ fp32 NT GEMM
-// C[m, n] = sum_k A[m, k] * B[n, k]. Block tile 128 x (32*NT), k-chunks of 32 staged in LDS.
-// Each wave owns 32 rows and NT 32x32 accumulator tiles of v_mfma_f32_32x32x2_f32.
-// In a k-chunk, lane half g (lanes 32g..32g+31) supplies contraction indices 16g..16g+15,
-// one per MFMA step, so each lane reads 16 contiguous floats of its A row and B row with
-// four 16-byte LDS loads; the same index map on both operands keeps the sum exact.
+// ============================================================================ NT GEMM
+// C[m, n] = sum_k A[m, k] * B[n, k] for fp32 A, B, C on the bf16 matrix cores.
+//
+// Each fp32 operand x is split into three bf16 parts x = h + m + l + r: h = bf16(x),
+// m = bf16(x - h), l = bf16(x - h - m), rounding to nearest even, with both subtractions exact
+// in fp32. Then |m| <= 2^-9 |x|, |l| <= 2^-18 |x| and |r| <= 2^-27 |x|. A product a b keeps the
+// six part products hh, hm, mh, hl, mm, lh; the dropped ones (ml, lm, ll) and the residues add
+// up to less than about 2^-25 |a b|, so each product carries fp32-level relative error. The
+// six 32x32x16 bf16 MFMAs take 192 cycles where the fp32 MFMA needs 512 for the same block.
+//
+// Block tile 128 x (32*NT), k-chunks of 32: the chunk's fp32 tiles come from global memory into
+// registers one chunk ahead, are split, and are stored as three bf16 planes per operand in
+// LDS (rows padded to 80 bytes: 16 lanes reading 16 bytes of 16 consecutive rows hit 16
+// distinct bank quads). Each wave owns 32 rows and NT 32x32 accumulator tiles.
+struct Bf16x4Planes {
+  bf16x4_t h, m, l;
+};
+__device__ __forceinline__ Bf16x4Planes split3(f32x4_t x) {
+  Bf16x4Planes p;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    const float r1 = x[e] - (float)h;
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - (float)m;
+    p.h[e] = h;
+    p.m[e] = m;
+    p.l[e] = (__bf16)r2;
+  }
+  return p;
+}
+
 template <int NT>
-__global__ __launch_bounds__(256) void gemm_nt_f32_kernel(const float* __restrict__ A,
-                                                          const float* __restrict__ B,
-                                                          float* __restrict__ C, int64_t M, int N,
-                                                          int Kd, int ldc) {
-  constexpr int BM = 128, BN = 32 * NT, BK = 32, LDP = BK + 4;
-  __shared__ __attribute__((aligned(16))) float As[BM * LDP];
-  __shared__ __attribute__((aligned(16))) float Bs[BN * LDP];
+__global__ __launch_bounds__(256) void gemm_nt_split_kernel(const float* __restrict__ A,
+                                                            const float* __restrict__ B,
+                                                            float* __restrict__ C, int64_t M,
+                                                            int N, int Kd, int ldc) {
+  constexpr int BM = 128, BN = 32 * NT, BK = 32, LDA = 40;  // LDA: bf16 per padded row
+  __shared__ __attribute__((aligned(16))) __bf16 As[3][BM * LDA];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[3][BN * LDA];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, j = l & 31, g = l >> 5;
   const int64_t m0 = (int64_t)blockIdx.x * BM;
   const int n0 = blockIdx.y * BN;
@@ -53,30 +80,42 @@ __global__ __launch_bounds__(256) void gemm_nt_f32_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
-      *(f32x4_t*)&As[r * LDP + c] = ra[i];
+      const Bf16x4Planes pl = split3(ra[i]);
+      *(bf16x4_t*)&As[0][r * LDA + c] = pl.h;
+      *(bf16x4_t*)&As[1][r * LDA + c] = pl.m;
+      *(bf16x4_t*)&As[2][r * LDA + c] = pl.l;
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
-      *(f32x4_t*)&Bs[r * LDP + c] = rb[i];
+      const Bf16x4Planes pl = split3(rb[i]);
+      *(bf16x4_t*)&Bs[0][r * LDA + c] = pl.h;
+      *(bf16x4_t*)&Bs[1][r * LDA + c] = pl.m;
+      *(bf16x4_t*)&Bs[2][r * LDA + c] = pl.l;
     }
     __syncthreads();
     if (k0 + BK < Kd) load(k0 + BK);
 
-    f32x4_t a4[4];
-    const float* ap = &As[(wave * 32 + j) * LDP + 16 * g];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a4[q] = *(const f32x4_t*)(ap + 4 * q);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t a[3];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4_t b4[4];
-      const float* bp = &Bs[(t * 32 + j) * LDP + 16 * g];
+      for (int p = 0; p < 3; ++p)
+        a[p] = *(const bf16x8_t*)&As[p][(wave * 32 + j) * LDA + ks * 16 + 8 * g];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b4[q] = *(const f32x4_t*)(bp + 4 * q);
+      for (int t = 0; t < NT; ++t) {
+        bf16x8_t b[3];
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[s >> 2][s & 3], b4[s >> 2][s & 3], acc[t],
-                                                      0, 0, 0);
+        for (int p = 0; p < 3; ++p)
+          b[p] = *(const bf16x8_t*)&Bs[p][(t * 32 + j) * LDA + ks * 16 + 8 * g];
+        // small terms first
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc[t], 0, 0, 0);
+      }
     }
   }
 
@@ -97,14 +136,14 @@ hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int64_t 
   dim3 block(256);
   int64_t mb = (M + 127) / 128;
   if (N <= 32) {
-    hipLaunchKernelGGL(gemm_nt_f32_kernel<1>, dim3(mb, (N + 31) / 32), block, 0, stream, A, B, C, M,
-                       N, Kd, ldc);
-  } else if (N <= 64) {
-    hipLaunchKernelGGL(gemm_nt_f32_kernel<2>, dim3(mb, (N + 63) / 64), block, 0, stream, A, B, C, M,
-                       N, Kd, ldc);
-  } else {
-    hipLaunchKernelGGL(gemm_nt_f32_kernel<4>, dim3(mb, (N + 127) / 128), block, 0, stream, A, B, C,
+    hipLaunchKernelGGL(gemm_nt_split_kernel<1>, dim3(mb, (N + 31) / 32), block, 0, stream, A, B, C,
                        M, N, Kd, ldc);
+  } else if (N <= 64) {
+    hipLaunchKernelGGL(gemm_nt_split_kernel<2>, dim3(mb, (N + 63) / 64), block, 0, stream, A, B, C,
+                       M, N, Kd, ldc);
+  } else {
+    hipLaunchKernelGGL(gemm_nt_split_kernel<4>, dim3(mb, (N + 127) / 128), block, 0, stream, A, B,
+                       C, M, N, Kd, ldc);
   }
   return hipGetLastError();
 }
