@@ -131,6 +131,55 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int K, int T, int32_t* til
   return hipGetLastError();
 }
 
+// ============================================================================ work plan
+// plan[item] = (q0, q1, kv_lo, ntiles) of group-pass work item `item`, for item < w_max (items
+// past the last real one get q0 == q1). Items are (segment, query tile) in segment order, the
+// heaviest tiles of a segment first; ntiles stops at the first key tile whose pairs all fall
+// inside the window for the tile's last query (positions ascend within a segment).
+__global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restrict__ seg_off,
+                                                         const int32_t* __restrict__ tile_pre,
+                                                         const i32x4_t* __restrict__ kinfo, int K,
+                                                         int T, int window, int w_max,
+                                                         i32x4_t* __restrict__ plan) {
+  constexpr int KT_ = 64;
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= w_max) return;
+  i32x4_t p = {0, 0, 0, 0};
+  if (item < tile_pre[K]) {
+    int lo = 0, hi = K - 1;  // largest g with tile_pre[g] <= item (a non-empty segment)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_pre[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    const int nt = tile_pre[lo + 1] - tile_pre[lo];
+    const int t = nt - 1 - (item - tile_pre[lo]);
+    const int s_lo = seg_off[lo], s_hi = seg_off[lo + 1];
+    const int q0 = s_lo + t * T, q1 = min(q0 + T, s_hi);
+    const int tpos_hi = kinfo[q1 - 1][0];
+    int lo_t = 0, hi_t = (q1 - 1 - s_lo) / KT_ + 1;
+    while (lo_t < hi_t) {
+      const int mid = (lo_t + hi_t) >> 1;
+      if (tpos_hi - kinfo[s_lo + mid * KT_][0] < window) hi_t = mid;
+      else lo_t = mid + 1;
+    }
+    p = i32x4_t{q0, q1, s_lo, lo_t};
+  }
+  plan[item] = p;
+}
+
+int attn_work_items(int64_t nk, int T, int K) { return (int)((nk + T - 1) / T + K); }
+
+hipError_t launch_plan_tiles(const int32_t* offsets, const int32_t* tile_pre, const int32_t* kinfo,
+                             const AttnShape& s, int32_t* plan, hipStream_t stream) {
+  const int T = attn_tile_tokens(s.G);
+  const int w_max = attn_work_items(s.nk, T, s.K);
+  const int window = (int)(s.window < s.n ? s.window : s.n);
+  hipLaunchKernelGGL(plan_tiles_kernel, dim3((w_max + 255) / 256), dim3(256), 0, stream, offsets,
+                     tile_pre, (const i32x4_t*)kinfo, s.K, T, window, w_max, (i32x4_t*)plan);
+  return hipGetLastError();
+}
+
 // ============================================================================ flash kernel
 struct FlashArgs {
   const uint16_t* q;  // [n, Hq, DH] in token order (group pass: row of slot s is kinfo[s].x)
@@ -149,6 +198,8 @@ struct FlashArgs {
   const int32_t* seg_off;   // group: [K+1]
   const int32_t* tile_pre;  // group: [K+1]
   const i32x4_t* kinfo;     // group: per slot (position, lower groups, -1 padded)
+  const i32x4_t* plan;      // group: per work item (q0, q1, kv_lo, ntiles); q0 == q1: none
+  int w_max;                // group: work items per kv head (upper bound)
   int K;
   int tiles_per_head;       // window: ceil(n / T)
 };
@@ -225,27 +276,21 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------------------------------------------------------- work item
-  const int W = GROUP ? a.tile_pre[a.K] : a.tiles_per_head;
+  const int W = GROUP ? a.w_max : a.tiles_per_head;
   const int64_t comb = xcd_remap(blockIdx.x, (int64_t)a.Hkv * W);
   if (comb < 0) return;
   const int h = (int)(comb / W);
   const int item = (int)(comb - (int64_t)h * W);
   const int window = a.window;
 
-  int q0, q1, kv_lo;  // slots (group) or tokens (window); all below 2^31
+  int q0, q1, kv_lo, ntiles;  // slots (group) or tokens (window); all below 2^31
   if constexpr (GROUP) {
-    int lo = 0, hi = a.K - 1;  // largest g with tile_pre[g] <= item (a non-empty segment)
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (a.tile_pre[mid] <= item) lo = mid;
-      else hi = mid - 1;
-    }
-    const int nt = a.tile_pre[lo + 1] - a.tile_pre[lo];
-    const int t = nt - 1 - (item - a.tile_pre[lo]);  // heaviest tiles of a segment first
-    const int s_lo = a.seg_off[lo], s_hi = a.seg_off[lo + 1];
-    q0 = s_lo + t * a.T;
-    q1 = min(q0 + a.T, s_hi);
-    kv_lo = s_lo;
+    const i32x4_t pl = a.plan[item];  // one load replaces the searches of the work item
+    q0 = pl[0];
+    q1 = pl[1];
+    kv_lo = pl[2];
+    ntiles = pl[3];
+    if (q0 >= q1) return;
   } else {
     q0 = item * a.T;
     q1 = (int)min((int64_t)q0 + a.T, a.n);
@@ -265,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   const int wq_hi = min(q0 + wt0 + wtn, q1) - 1;
   const bool wave_active = wq_hi >= wq_lo;
 
-  int qpos = 0, wpos_lo = 0, wpos_hi = 0, tpos_hi = 0;
+  int qpos = 0, wpos_lo = 0, wpos_hi = 0;
   int qlow[3] = {-2, -2, -2};
   if constexpr (GROUP) {
     if (qvalid) {
@@ -278,7 +323,6 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       wpos_lo = a.kinfo[wq_lo][0];
       wpos_hi = a.kinfo[wq_hi][0];
     }
-    tpos_hi = a.kinfo[kv_hi][0];
   } else {
     qpos = qi;
   }
@@ -300,29 +344,15 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     for (int j = 0; j < MKS; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qm[j][e] = (__bf16)(16 * j + 8 * hg + e == tw ? kMaskBias : 0.f);
-    if (tid < 32) {
-      const int t = tid, qt = q0 + t;
-      i32x4_t info = {0, -2, -2, -2};
-      if (t < a.T && qt < q1) info = a.kinfo[qt];
-#pragma unroll
-      for (int c = 0; c < NLOW; ++c) qlow_s[c][t] = (t < a.T && qt < q1 && info[1 + c] >= 0) ? info[1 + c] : -2;
-    }
+  }
+  // the tile's query tokens' records (for the lower-group table written after the first wait)
+  i32x4_t tok_rec = {0, -2, -2, -2};
+  if constexpr (MKS > 0) {
+    if (tid < 32 && tid < a.T && q0 + tid < q1) tok_rec = a.kinfo[q0 + tid];
   }
 
   // ---------------------------------------------------------------- kv tile range
-  int ntiles;
-  if constexpr (GROUP) {
-    // tiles up to the first one whose pairs all fall inside the window (positions ascend)
-    int lo_t = 0, hi_t = (kv_hi - kv_lo) / KT + 1;
-    while (lo_t < hi_t) {
-      int mid = (lo_t + hi_t) >> 1;
-      if (tpos_hi - a.kinfo[kv_lo + mid * KT][0] < window) hi_t = mid;
-      else lo_t = mid + 1;
-    }
-    ntiles = lo_t;
-  } else {
-    ntiles = window > 0 ? (kv_hi - kv_lo) / KT + 1 : 0;
-  }
+  if constexpr (!GROUP) ntiles = window > 0 ? (kv_hi - kv_lo) / KT + 1 : 0;
 
   f32x16_t oacc[ND];
 #pragma unroll
@@ -595,14 +625,23 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     }
   };
 
-  if constexpr (MKS > 0) __syncthreads();  // qlow_s is read by every tile's bias rows
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // query rows and records are in registers
+  // group pass: the first tile's copies go out with the query-row loads and one wait covers
+  // both (measured neutral to slightly worse for the window pass, which keeps two waits)
+  if constexpr (!GROUP) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (ntiles > 0) issue_tile(kv_lo, smem[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (MKS > 0) {
+    if (tid < 32) {
+#pragma unroll
+      for (int c = 0; c < NLOW; ++c) qlow_s[c][tid] = tok_rec[1 + c] >= 0 ? tok_rec[1 + c] : -2;
+    }
+    __syncthreads();  // qlow_s is read by every tile's bias rows
+  }
   if (ntiles > 0) {
-    issue_tile(kv_lo, smem[0]);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     finish_tile(smem[0]);
     __syncthreads();
   }
+
   // unrolled by two so each copy addresses one LDS buffer through immediates
   auto step = [&](int it, auto parity) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
@@ -642,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     // merge the window part with this token's group parts by log-sum-exp, in token order
     typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
     float Lr[4];
-    int64_t srow[4];
+    int srow[4];
     float M = L_own;
     for (int r = 0; r < a.top_k; ++r) {
       const int sl = a.slot[(int64_t)qi * a.top_k + r];
@@ -671,7 +710,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     for (int r = 0; r < a.top_k; ++r) {
       if (Lr[r] == -INFINITY) continue;
       const float c = wr[r] * inv_den;
-      const _Float16* gp = a.og + (srow[r] * a.Hq + hq) * DH + 4 * hg;
+      const _Float16* gp = a.og + ((int64_t)srow[r] * a.Hq + hq) * DH + 4 * hg;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -711,8 +750,8 @@ static void flash_dispatch_group(const FlashArgs& fa, int dh, int mks, int64_t b
 
 hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
                                   const int32_t* offsets, const int32_t* tile_pre,
-                                  const int32_t* kinfo, const AttnShape& s, _Float16* og,
-                                  float* lseg, hipStream_t stream) {
+                                  const int32_t* kinfo, const int32_t* plan, const AttnShape& s,
+                                  _Float16* og, float* lseg, hipStream_t stream) {
   FlashArgs fa{};
   fa.q = q;
   fa.k = kg;
@@ -729,11 +768,12 @@ hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const u
   fa.seg_off = offsets;
   fa.tile_pre = tile_pre;
   fa.kinfo = (const i32x4_t*)kinfo;
+  fa.plan = (const i32x4_t*)plan;
   fa.K = s.K;
   fa.top_k = s.top_k;
   // upper bound on the tiles of all segments: sum of ceil(size / T) <= ceil(nk / T) + K
-  const int64_t w_max = (s.nk + fa.T - 1) / fa.T + s.K;
-  const int64_t blocks = xcd_grid((int64_t)s.Hkv * w_max);
+  fa.w_max = attn_work_items(s.nk, fa.T, s.K);
+  const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.w_max);
   if (blocks <= 0) return hipSuccess;
   // The ownership rule runs as an MFMA bias when a wave's rows span at most 32 tokens and the
   // scaled bias (-2^100 * scale * log2 e) still drives exp2 to zero; else per-element compares.

@@ -70,6 +70,7 @@ struct AttnWs {
   float* lseg;
   int32_t* kinfo;
   int32_t* tile_pre;
+  int32_t* plan;
 };
 
 // Gathered K/V per membership, the per-membership key records, the group pass's fp16
@@ -84,6 +85,9 @@ size_t attn_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k
   w.lseg = c.take<float>((size_t)nk * Hq);
   w.kinfo = c.take<int32_t>((size_t)nk * 4);
   w.tile_pre = c.take<int32_t>((size_t)K + 1);
+  const int G = Hq / Hkv > 1 ? Hq / Hkv : 1;  // the size query takes unvalidated head counts
+  const int T = attn_tile_tokens(G) > 1 ? attn_tile_tokens(G) : 1;
+  w.plan = c.take<int32_t>((size_t)4 * attn_work_items(nk, T, K));
   if (out) *out = w;
   return c.used;
 }
@@ -257,10 +261,12 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_tile_prefix(offsets, K, attn_tile_tokens(s.G), w.tile_pre, st);
+  if (e == hipSuccess) e = launch_plan_tiles(offsets, w.tile_pre, w.kinfo, s, w.plan, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess)
-    e = launch_group_attention(q, w.kg, w.vg, offsets, w.tile_pre, w.kinfo, s, w.og, w.lseg, st);
+    e = launch_group_attention(q, w.kg, w.vg, offsets, w.tile_pre, w.kinfo, w.plan, s, w.og,
+                               w.lseg, st);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess)

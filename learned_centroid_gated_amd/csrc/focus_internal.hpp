@@ -83,10 +83,14 @@ hipError_t launch_gather_kv(const uint16_t* k, const uint16_t* v, const int32_t*
                             uint16_t* kg, uint16_t* vg, int32_t* kinfo, hipStream_t stream);
 hipError_t launch_tile_prefix(const int32_t* offsets, int K, int T, int32_t* tile_pre,
                               hipStream_t stream);
+// group-pass work items per kv head (an upper bound: ceil(nk / T) + K)
+int attn_work_items(int64_t nk, int T, int K);
+hipError_t launch_plan_tiles(const int32_t* offsets, const int32_t* tile_pre, const int32_t* kinfo,
+                             const AttnShape& s, int32_t* plan, hipStream_t stream);
 hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
                                   const int32_t* offsets, const int32_t* tile_pre,
-                                  const int32_t* kinfo, const AttnShape& s, _Float16* og,
-                                  float* lseg, hipStream_t stream);
+                                  const int32_t* kinfo, const int32_t* plan, const AttnShape& s,
+                                  _Float16* og, float* lseg, hipStream_t stream);
 hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    const _Float16* og, const float* lseg, const int32_t* slot,
                                    const AttnShape& s, uint16_t* out, float* lse,
