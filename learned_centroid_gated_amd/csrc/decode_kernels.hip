@@ -20,27 +20,126 @@
 
 namespace focus {
 
-constexpr int kDecChunk = 256;   // list entries resolved per pass
 constexpr int kDecHeads = 4;     // query heads per block
+constexpr int kDecInfo = 12;     // per-sequence plan: lo, nl, -, then (segment start, count) x 4
 
 int decode_splits(const DecodeShape& s) {
   (void)s;
   return 16;
 }
 
+// ============================================================================ plan
+// info[b] = (lo, nl, 0, seg_lo_0, cnt_0, ..., seg_lo_3, cnt_3): the window is positions
+// lo .. lo + nl - 1; query group r contributes the cnt_r members of its segment from index
+// seg_lo_r on, those at positions <= p - w'. One wave per (sequence, query group) finds the
+// boundary with a 64-ary search: each step probes 64 evenly spaced members at once.
+__global__ __launch_bounds__(64) void decode_seg_kernel(const int32_t* __restrict__ q_groups,
+                                                        const int32_t* __restrict__ cache_len,
+                                                        const int32_t* __restrict__ cache_off,
+                                                        const int32_t* __restrict__ cache_idx,
+                                                        int64_t Lmax, int K, int top_k,
+                                                        int64_t window,
+                                                        int32_t* __restrict__ info) {
+  const int b = blockIdx.x / top_k, r = blockIdx.x % top_k, l = threadIdx.x;
+  int64_t L = cache_len[b];
+  if (L < 1) L = 1;
+  if (L > Lmax) L = Lmax;
+  const int64_t p = L - 1;
+  const int64_t wl = window > 1 ? window : 1;
+  const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
+  int32_t* inf = info + (int64_t)b * kDecInfo;
+  if (r == 0 && l == 0) {
+    inf[0] = (int32_t)lo;
+    inf[1] = (int32_t)(p - lo + 1);
+    inf[2] = 0;
+    for (int rr = top_k; rr < 4; ++rr) {
+      inf[3 + 2 * rr] = 0;
+      inf[4 + 2 * rr] = 0;
+    }
+  }
+  const int g = q_groups[(int64_t)b * top_k + r];
+  int64_t s0 = 0, cnt = 0;
+  if (g >= 0 && g < K) {
+    const int32_t* off = cache_off + (int64_t)b * (K + 1);
+    const int32_t* cidx = cache_idx + (int64_t)b * Lmax * top_k;
+    s0 = off[g];
+    // first member index in [s0, s1) at a position > p - wl (positions ascend in a segment).
+    // Invariant: members below lo_i are at or before the boundary, members from hi_i on after.
+    // Lane l probes lo_i + span*l/64; the probes at or before the boundary form a prefix of
+    // n_le lanes, so the answer lies after the last of them and at or before the next.
+    const int64_t thr = p - wl;
+    int64_t lo_i = s0, hi_i = off[g + 1];
+    while (lo_i < hi_i) {
+      const int64_t span = hi_i - lo_i;
+      const bool le = (int64_t)cidx[lo_i + (span * l) / 64] <= thr;
+      const int n_le = __popcll(__ballot(le));
+      if (n_le == 0) break;  // even lo_i is past the boundary
+      if (n_le < 64) hi_i = lo_i + (span * n_le) / 64;
+      lo_i = lo_i + (span * (n_le - 1)) / 64 + 1;
+    }
+    cnt = lo_i - s0;
+  }
+  if (l == 0) {
+    inf[3 + 2 * r] = (int32_t)s0;
+    inf[4 + 2 * r] = (int32_t)cnt;
+  }
+}
+
+// list[b][vi] = key position of virtual list entry vi, or -1 when the entry is a member of a
+// query group that a lower shared query group owns (so every allowed key is listed once).
+__global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restrict__ q_groups,
+                                                          const int32_t* __restrict__ cache_groups,
+                                                          const int32_t* __restrict__ cache_idx,
+                                                          const int32_t* __restrict__ info,
+                                                          int64_t Lmax, int K, int top_k,
+                                                          int64_t per_seq,
+                                                          int32_t* __restrict__ list) {
+  const int64_t chunks = (per_seq + 255) / 256;
+  const int b = (int)(blockIdx.x / chunks);
+  const int64_t vi = (blockIdx.x % chunks) * 256 + threadIdx.x;
+  const int32_t* inf = info + (int64_t)b * kDecInfo;
+  const int64_t lo = inf[0], nl = inf[1];
+  int64_t total = nl;
+  for (int r = 0; r < top_k; ++r) total += inf[4 + 2 * r];
+  if (vi >= total) return;
+  int pos = -1;
+  if (vi < nl) {
+    pos = (int)(lo + vi);
+  } else {
+    int qg[4];
+    for (int r = 0; r < top_k; ++r) qg[r] = q_groups[(int64_t)b * top_k + r];
+    int64_t rem = vi - nl;
+    for (int r = 0; r < top_k; ++r) {
+      const int64_t cnt = inf[4 + 2 * r];
+      if (rem < cnt) {
+        const int cand = cache_idx[(int64_t)b * Lmax * top_k + inf[3 + 2 * r] + rem];
+        // owned by g_r unless the key also holds a lower query group
+        bool owned = true;
+        const int32_t* kg = cache_groups + ((int64_t)b * Lmax + cand) * top_k;
+        for (int r2 = 0; r2 < top_k; ++r2) {
+          const int g2 = qg[r2];
+          if (g2 >= 0 && g2 < K && g2 < qg[r])
+            for (int r3 = 0; r3 < top_k; ++r3) owned = owned && kg[r3] != g2;
+        }
+        pos = owned ? cand : -1;
+        break;
+      }
+      rem -= cnt;
+    }
+  }
+  list[(int64_t)b * per_seq + vi] = pos;
+}
+
 struct DecodeArgs {
   const uint16_t* q;
-  const int32_t* q_groups;
   const uint16_t* kc;
   const uint16_t* vc;
-  const int32_t* cache_len;
-  const int32_t* cache_groups;
-  const int32_t* cache_off;
-  const int32_t* cache_idx;
+  const int32_t* info;
+  const int32_t* list;
+  int64_t per_seq;  // list capacity per sequence
   int B;
   int64_t Lmax;
-  int Hq, Hkv, G, K, top_k, splits, hpb;  // hpb: query heads per block (<= kDecHeads)
-  int64_t window;
+  int Hq, Hkv, G, top_k, splits, hpb;  // hpb: query heads per block (<= kDecHeads)
   float sl2;
   float* part_o;   // [B, Hq, splits, DH] unnormalised
   float* part_ml;  // [B, Hq, splits, 2] (running max in log2 units, sum)
@@ -53,13 +152,19 @@ __device__ __forceinline__ float group_sum(float x) {  // sum over the lane's al
   return x;
 }
 
+// The sequence's resolved key list is cut into `splits` contiguous pieces per (sequence, group
+// of up to 4 query heads of one kv head). Every 16-lane group takes one key at a time: each lane
+// holds 8 dims of the query heads in registers and reads one coalesced 16-byte chunk of the
+// key's K and V rows, the dot products are reduced across the 16 lanes, and a running
+// (max, sum, O) per head absorbs the key. A lane group keeps U keys' rows in flight and loads
+// the positions of its next U keys before absorbing the current ones.
 template <int DH>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
   constexpr int CHK = DH / 8;          // 16-byte chunks per row: lanes per key
   constexpr int KPW = kWave / CHK;     // keys per wave instruction
   constexpr int NG = 4 * KPW;          // lane groups per block
   constexpr int HD = kDecHeads;
-  __shared__ int kpos[kDecChunk];
+  constexpr int U = 4;                 // keys in flight per lane group
   __shared__ float red_o[NG][HD][DH];
   __shared__ float red_ml[NG][HD][2];
 
@@ -72,40 +177,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const int hq0 = hgrp * a.hpb, h = hq0 / a.G;
   const int nh = a.hpb;
 
-  int64_t L = a.cache_len[b];
-  if (L < 1) L = 1;
-  if (L > a.Lmax) L = a.Lmax;
-  const int64_t p = L - 1;
-  const int64_t wl = a.window > 1 ? a.window : 1;
-  const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
-  const int64_t nl = p - lo + 1;
-
-  // query groups, segment starts and the number of far members per group
-  int qg[4];
-  int64_t seg_lo[4], cnt[4];
-  const int32_t* off = a.cache_off + (int64_t)b * (a.K + 1);
-  const int32_t* cidx = a.cache_idx + (int64_t)b * a.Lmax * a.top_k;
-  int64_t total = nl;
-  for (int r = 0; r < a.top_k; ++r) {
-    int g = a.q_groups[(int64_t)b * a.top_k + r];
-    qg[r] = g;
-    seg_lo[r] = 0;
-    cnt[r] = 0;
-    if (g < 0 || g >= a.K) continue;
-    int64_t s0 = off[g], s1 = off[g + 1];
-    int64_t lo_i = s0, hi_i = s1;  // first member at a position > p - wl
-    while (lo_i < hi_i) {
-      int64_t mid = (lo_i + hi_i) >> 1;
-      if ((int64_t)cidx[mid] <= p - wl) lo_i = mid + 1;
-      else hi_i = mid;
-    }
-    seg_lo[r] = s0;
-    cnt[r] = lo_i - s0;
-    total += cnt[r];
-  }
+  const int32_t* inf = a.info + (int64_t)b * kDecInfo;
+  int64_t total = inf[1];
+  for (int r = 0; r < a.top_k; ++r) total += inf[4 + 2 * r];
   const int64_t per = (total + a.splits - 1) / a.splits;
   const int64_t v0 = (int64_t)sp * per;
   const int64_t v1 = v0 + per < total ? v0 + per : total;
+  const int32_t* lst = a.list + (int64_t)b * a.per_seq;
 
   // this lane's slice of the query heads, pre-scaled to log2 units
   float qf[HD][8];
@@ -132,84 +210,60 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const uint16_t* kbase = a.kc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
   const uint16_t* vbase = a.vc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
 
-  for (int64_t c0 = v0; c0 < v1; c0 += kDecChunk) {
-    // ---- resolve list entries c0 + tid into key positions (-1: not this query's key)
-    {
-      const int64_t vi = c0 + tid;
-      int pos = -1;
-      if (vi < v1) {
-        if (vi < nl) {
-          pos = (int)(lo + vi);
-        } else {
-          int64_t rem = vi - nl;
-          for (int r = 0; r < a.top_k; ++r) {
-            if (rem < cnt[r]) {
-              const int cand = cidx[seg_lo[r] + rem];
-              // owned by g_r unless the key also holds a lower query group
-              bool owned = true;
-              const int32_t* kg = a.cache_groups + ((int64_t)b * a.Lmax + cand) * a.top_k;
-              for (int r2 = 0; r2 < a.top_k; ++r2) {
-                const int g2 = qg[r2];
-                if (g2 >= 0 && g2 < a.K && g2 < qg[r])
-                  for (int r3 = 0; r3 < a.top_k; ++r3) owned = owned && kg[r3] != g2;
-              }
-              pos = owned ? cand : -1;
-              break;
-            }
-            rem -= cnt[r];
-          }
-        }
-      }
-      kpos[tid] = pos;
+  // entries v0 + grp + k * NG of the piece, U at a time
+  int pn[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = v0 + grp + (int64_t)u * NG;
+    pn[u] = j < v1 ? lst[j] : -1;
+  }
+  for (int64_t j0 = v0 + grp; j0 < v1; j0 += (int64_t)U * NG) {
+    int pk[U];
+    i32x4_t kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      pk[u] = pn[u];
+      const int64_t row = pk[u] >= 0 ? pk[u] : 0;
+      kr[u] = *(const i32x4_t*)(kbase + row * kv_stride);
+      vr[u] = *(const i32x4_t*)(vbase + row * kv_stride);
     }
-    __syncthreads();
-    // ---- lane group grp absorbs entries grp, grp + NG, ... of this chunk, 4 at a time
-    const int nent = (int)(v1 - c0 < kDecChunk ? v1 - c0 : kDecChunk);
-    for (int j0 = grp; j0 < nent; j0 += 4 * NG) {
-      int pk[4];
-      i32x4_t kr[4], vr[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + u * NG;
-        pk[u] = j < nent ? kpos[j] : -1;
-        const int64_t row = pk[u] >= 0 ? pk[u] : 0;
-        kr[u] = *(const i32x4_t*)(kbase + row * kv_stride);
-        vr[u] = *(const i32x4_t*)(vbase + row * kv_stride);
+    for (int u = 0; u < U; ++u) {  // positions of the next U keys, behind this batch's rows
+      const int64_t j = j0 + (int64_t)(U + u) * NG;
+      pn[u] = j < v1 ? lst[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (pk[u] < 0) continue;  // uniform within the lane group
+      float kf[8], vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = __uint_as_float((uint32_t)kr[u][e] << 16);
+        kf[2 * e + 1] = __uint_as_float((uint32_t)kr[u][e] & 0xffff0000u);
+        vf[2 * e] = __uint_as_float((uint32_t)vr[u][e] << 16);
+        vf[2 * e + 1] = __uint_as_float((uint32_t)vr[u][e] & 0xffff0000u);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pk[u] < 0) continue;  // uniform within the lane group
-        float kf[8], vf[8];
+      for (int hh = 0; hh < HD; ++hh) {
+        if (hh >= nh) break;
+        float sdot = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = __uint_as_float((uint32_t)kr[u][e] << 16);
-          kf[2 * e + 1] = __uint_as_float((uint32_t)kr[u][e] & 0xffff0000u);
-          vf[2 * e] = __uint_as_float((uint32_t)vr[u][e] << 16);
-          vf[2 * e + 1] = __uint_as_float((uint32_t)vr[u][e] & 0xffff0000u);
+        for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(qf[hh][e], kf[e], sdot);
+        sdot = group_sum<CHK>(sdot);
+        // lazy running max: rescale only when the score passes the reference by 2^8
+        if (sdot > m_run[hh] + 8.f) {
+          const float alpha = m_run[hh] == -INFINITY ? 0.f : fast_exp2(m_run[hh] - sdot);
+          l_run[hh] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
+          m_run[hh] = sdot;
         }
+        const float pw = fast_exp2(sdot - m_run[hh]);
+        l_run[hh] += pw;
 #pragma unroll
-        for (int hh = 0; hh < HD; ++hh) {
-          if (hh >= nh) break;
-          float sdot = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(qf[hh][e], kf[e], sdot);
-          sdot = group_sum<CHK>(sdot);
-          // lazy running max: rescale only when the score passes the reference by 2^8
-          if (sdot > m_run[hh] + 8.f) {
-            const float alpha = m_run[hh] == -INFINITY ? 0.f : fast_exp2(m_run[hh] - sdot);
-            l_run[hh] *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
-            m_run[hh] = sdot;
-          }
-          const float pw = fast_exp2(sdot - m_run[hh]);
-          l_run[hh] += pw;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pw, vf[e], o[hh][e]);
-        }
+        for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pw, vf[e], o[hh][e]);
       }
     }
-    __syncthreads();
   }
 
   // ---- merge the lane groups' states and write this block's partial per head
@@ -280,26 +334,31 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(const float* __restr
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
-                         float* part_o, float* part_ml, uint16_t* out, float* lse,
-                         hipStream_t stream) {
+                         int32_t* info, int32_t* list, float* part_o, float* part_ml,
+                         uint16_t* out, float* lse, hipStream_t stream) {
+  const int64_t per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
+  hipLaunchKernelGGL(decode_seg_kernel, dim3((int64_t)s.B * s.top_k), dim3(64), 0, stream,
+                     q_groups, cache_len, cache_off, cache_idx, s.Lmax, s.K, s.top_k, s.window,
+                     info);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * ((per_seq + 255) / 256)), dim3(256),
+                     0, stream, q_groups, cache_groups, cache_idx, info, s.Lmax, s.K, s.top_k,
+                     per_seq, list);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   DecodeArgs a{};
   a.q = q;
-  a.q_groups = q_groups;
   a.kc = kc;
   a.vc = vc;
-  a.cache_len = cache_len;
-  a.cache_groups = cache_groups;
-  a.cache_off = cache_off;
-  a.cache_idx = cache_idx;
+  a.info = info;
+  a.list = list;
+  a.per_seq = per_seq;
   a.B = s.B;
   a.Lmax = s.Lmax;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.G = s.G;
-  a.K = s.K;
   a.top_k = s.top_k;
   a.splits = s.splits;
-  a.window = s.window;
   a.sl2 = s.scale * kLog2e;
   a.part_o = part_o;
   a.part_ml = part_ml;

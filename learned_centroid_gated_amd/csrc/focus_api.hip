@@ -285,18 +285,32 @@ int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
 }
 
 // ============================================================================ decode
+// Per-sequence plan (12 ints), each sequence's resolved key list (at most top_k * Lmax
+// entries), and the split partials (O and (max, sum) per query head and split).
+struct DecodeWs {
+  int32_t* info;
+  int32_t* list;
+  float* part_o;
+  float* part_ml;
+};
+size_t decode_carve(void* ws, int B, int64_t Lmax, int Hq, int d_head, int top_k, int splits,
+                    DecodeWs* out) {
+  Carver c(ws);
+  DecodeWs w{};
+  w.info = c.take<int32_t>((size_t)B * 12);
+  w.list = c.take<int32_t>((size_t)B * Lmax * top_k);
+  w.part_o = c.take<float>((size_t)B * Hq * splits * d_head);
+  w.part_ml = c.take<float>((size_t)B * Hq * splits * 2);
+  if (out) *out = w;
+  return c.used;
+}
+
 size_t focus_decode_workspace_size(int B, int64_t Lmax, int Hq, int Hkv, int d_head, int K,
                                    int top_k) {
-  (void)Lmax;
   (void)K;
-  (void)top_k;
-  if (B < 0 || Hq < 1 || Hkv < 1 || d_head < 1) return 0;
+  if (B < 0 || Lmax < 1 || Hq < 1 || Hkv < 1 || d_head < 1 || top_k < 1) return 0;
   DecodeShape s{};
-  const int splits = decode_splits(s);
-  Carver c(nullptr);
-  c.take<float>((size_t)B * Hq * splits * d_head);
-  c.take<float>((size_t)B * Hq * splits * 2);
-  return c.used;
+  return decode_carve(nullptr, B, Lmax, Hq, d_head, top_k, decode_splits(s), nullptr);
 }
 
 int focus_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_cache,
@@ -333,12 +347,11 @@ int focus_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_c
   s.window = window;
   s.scale = sc;
   s.splits = decode_splits(s);
-  Carver c(workspace);
-  float* part_o = c.take<float>((size_t)B * Hq * s.splits * d_head);
-  float* part_ml = c.take<float>((size_t)B * Hq * s.splits * 2);
+  DecodeWs w;
+  decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
   return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
-                                  cache_offsets, cache_idx, s, part_o, part_ml, out, lse,
-                                  (hipStream_t)stream));
+                                  cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
+                                  w.part_ml, out, lse, (hipStream_t)stream));
 }
 
 }  // extern "C"
