@@ -257,7 +257,8 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kMaskBias = -0x1p100f;   // ownership bias of an excluded pair (before scaling)
 constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully masked rows
 
-// NLOW = top_k - 1 lower groups per membership matter for the ownership rule (group pass).
+// NLOW = top_k - 1: lower groups per membership that matter for the ownership rule (group
+// pass), and top_k - 1 for the window pass, whose merge reads top_k group parts per token.
 // MKS = 16-token k-steps of the MFMA ownership bias (0: per-element compare instead).
 template <int DH, bool GROUP, int NLOW, int MKS>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
@@ -269,6 +270,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   constexpr int ND = DH / 32;            // 32-wide output tiles over the head dimension
   constexpr int RB = 2 * DH;             // bytes per key row
   static_assert(MKS == 0 || (GROUP && NLOW > 0), "ownership bias only in the group pass");
+  static_assert(NLOW >= 0 && NLOW <= 3, "top_k is 1 to 4");
   __shared__ __attribute__((aligned(1024))) Smem smem[2];  // double buffer: one barrier per tile
   __shared__ __attribute__((aligned(16))) int qlow_s[3][32];  // MKS > 0: query tokens' lower groups, -2 if none
 
@@ -660,75 +662,140 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
 
   // ---------------------------------------------------------------- epilogue
-  if (!qvalid) return;
+  // Results leave through LDS. Each lane writes its row's values in the accumulator layout and
+  // reads back 16 consecutive bytes of one row, so every global access of the wave covers whole
+  // rows: in the accumulator layout one wave-wide access would touch 32 rows at 16 bytes each,
+  // and the vector memory path spends a cycle per cache line touched. Lanes of rows without a
+  // query stay active (shuffles and the window pass's barrier) but store nothing.
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
   const float L_own = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  constexpr int RPI = 64 / CH;  // rows per transposed access (CH lanes per row)
+  const int cl = l % CH;        // this lane's 16-byte chunk of the row in transposed accesses
   // Oᵀ accumulator layout: lane holds dims d*32 + 8*g4 + 4*hg + 0..3 of its query row
   if constexpr (GROUP) {
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    // smem[ntiles & 1] is not the last tile's buffer: every wave finished reading it before the
+    // loop's last barrier and no copy targets it since, so it needs no further barrier
+    char* ep = (char*)&smem[ntiles & 1] + wave * (32 * RB);  // 32 fp16 rows of 2 DH bytes
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    _Float16* op = a.og + ((int64_t)qi * a.Hq + hq) * DH;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-        f16x4_t x = {(_Float16)(oacc[d][4 * g4] * inv), (_Float16)(oacc[d][4 * g4 + 1] * inv),
-                     (_Float16)(oacc[d][4 * g4 + 2] * inv), (_Float16)(oacc[d][4 * g4 + 3] * inv)};
-        *(f16x4_t*)(op + d * 32 + g4 * 8 + 4 * hg) = x;
+        const f16x4_t x = {(_Float16)(oacc[d][4 * g4] * inv), (_Float16)(oacc[d][4 * g4 + 1] * inv),
+                           (_Float16)(oacc[d][4 * g4 + 2] * inv),
+                           (_Float16)(oacc[d][4 * g4 + 3] * inv)};
+        *(f16x4_t*)(ep + jq * RB + (((4 * d + g4) ^ (jq % CH)) * 16) + hg * 8) = x;
       }
-    if (hg == 0) a.lseg[(int64_t)qi * a.Hq + hq] = L_own;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + l / CH;
+      const int rr = wave * 32 + row;
+      const int qr = q0 + rr % a.T;
+      const i32x4_t x = *(const i32x4_t*)(ep + row * RB + ((cl ^ (row % CH)) * 16));
+      if (qr < q1)
+        *(i32x4_t*)(a.og + ((int64_t)qr * a.Hq + h * a.G + rr / a.T) * DH + 8 * cl) = x;
+    }
+    if (qvalid && hg == 0) a.lseg[(int64_t)qi * a.Hq + hq] = L_own;
   } else {
-    // merge the window part with this token's group parts by log-sum-exp, in token order
-    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-    float Lr[4];
-    int srow[4];
+    // merge the window part with this token's group parts by log-sum-exp, in token order;
+    // NLOW + 1 = top_k group parts per token
+    constexpr int TK = NLOW + 1;
+    float Lr[TK];
+    int srow[TK];
     float M = L_own;
-    for (int r = 0; r < a.top_k; ++r) {
-      const int sl = a.slot[(int64_t)qi * a.top_k + r];
+#pragma unroll
+    for (int r = 0; r < TK; ++r) {
+      const int sl = qvalid ? a.slot[(int64_t)qi * TK + r] : -1;
       srow[r] = sl;
       Lr[r] = sl >= 0 ? a.lseg[(int64_t)sl * a.Hq + hq] : -INFINITY;
       M = fmaxf(M, Lr[r]);
     }
-    float w_own = 0.f, den = 0.f, wr[4];
+    float w_own = 0.f, den = 0.f, cr[TK];
+#pragma unroll
+    for (int r = 0; r < TK; ++r) cr[r] = 0.f;
     if (M != -INFINITY) {
       w_own = L_own == -INFINITY ? 0.f : __expf(L_own - M);
       den = w_own;
-      for (int r = 0; r < a.top_k; ++r) {
-        wr[r] = Lr[r] == -INFINITY ? 0.f : __expf(Lr[r] - M);
-        den += wr[r];
+#pragma unroll
+      for (int r = 0; r < TK; ++r) {
+        cr[r] = Lr[r] == -INFINITY ? 0.f : __expf(Lr[r] - M);
+        den += cr[r];
       }
     }
     const float inv_den = den > 0.f ? 1.f / den : 0.f;
     const float c_own = l_tot > 0.f ? w_own * inv_den / l_tot : 0.f;
-    f32x4_t acc[ND][4];
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+    for (int r = 0; r < TK; ++r) cr[r] *= inv_den;
+
+    // group parts in the transposed layout, read in batches of NB rows per lane (all rows at
+    // top_k <= 2) whose loads are all issued before any is used; a row without that part reads
+    // slot 0 and its weight 0 leaves the sum untouched
+    typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+    constexpr int NI = 32 / RPI;
+    constexpr int NB = TK * NI <= 16 ? NI : NI / 2;
+    static_assert(NB * TK <= 16, "at most 16 loads in flight per lane");
+    char* ep = (char*)smem + wave * (32 * 4 * DH);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        acc[d][g4] = f32x4_t{oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2],
-                             oacc[d][4 * g4 + 3]} * c_own;
-    for (int r = 0; r < a.top_k; ++r) {
-      if (Lr[r] == -INFINITY) continue;
-      const float c = wr[r] * inv_den;
-      const _Float16* gp = a.og + ((int64_t)srow[r] * a.Hq + hq) * DH + 4 * hg;
+    for (int i0 = 0; i0 < NI; i0 += NB) {
+      f16x8_t gx[NB][TK];
+      float gc[NB][TK];
 #pragma unroll
-      for (int d = 0; d < ND; ++d)
+      for (int ib = 0; ib < NB; ++ib) {
+        const int row = (i0 + ib) * RPI + l / CH;
+        const int hr = h * a.G + (wave * 32 + row) / a.T;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f16x4_t x = *(const f16x4_t*)(gp + d * 32 + g4 * 8);
-          acc[d][g4] += c * f32x4_t{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        for (int r = 0; r < TK; ++r) {
+          gc[ib][r] = __shfl(cr[r], row, kWave);  // every lane takes part in the shuffles
+          const int sl = max(__shfl(srow[r], row, kWave), 0);
+          gx[ib][r] = *(const f16x8_t*)(a.og + ((int64_t)sl * a.Hq + hr) * DH + 8 * cl);
         }
-    }
-    uint16_t* outp = a.out + ((int64_t)qi * a.Hq + hq) * DH + 4 * hg;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4_t o4 = {to_bf16(acc[d][g4][0]), to_bf16(acc[d][g4][1]), to_bf16(acc[d][g4][2]),
-                       to_bf16(acc[d][g4][3])};
-        *(bf16x4_t*)(outp + d * 32 + g4 * 8) = o4;
       }
-    if (hg == 0) a.lse[(int64_t)qi * a.Hq + hq] = den > 0.f ? M + __logf(den) : -INFINITY;
+      if (i0 == 0) {
+        // the window part goes through LDS in fp32: 32 rows of 4 DH bytes per wave, spread over
+        // both tile buffers once every wave is done with them
+        static_assert(4 * 32 * 4 * DH <= 2 * sizeof(Smem), "merge staging exceeds the tile buffers");
+        __syncthreads();
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4_t x = f32x4_t{oacc[d][4 * g4], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2],
+                                      oacc[d][4 * g4 + 3]} * c_own;
+            *(f32x4_t*)(ep + jq * 4 * DH + (((8 * d + 2 * g4 + hg) ^ (jq & 15)) * 16)) = x;
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib) {
+        const int row = (i0 + ib) * RPI + l / CH;
+        const int rr = wave * 32 + row;
+        const int qr = q0 + rr % a.T;
+        const int hr = h * a.G + rr / a.T;
+        f32x4_t lo = *(const f32x4_t*)(ep + row * 4 * DH + (((2 * cl) ^ (row & 15)) * 16));
+        f32x4_t hi = *(const f32x4_t*)(ep + row * 4 * DH + (((2 * cl + 1) ^ (row & 15)) * 16));
+#pragma unroll
+        for (int r = 0; r < TK; ++r) {
+          const float c = gc[ib][r];
+          const f16x8_t x = gx[ib][r];
+          const f32x4_t nlo = lo + c * f32x4_t{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+          const f32x4_t nhi = hi + c * f32x4_t{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+          lo = c != 0.f ? nlo : lo;
+          hi = c != 0.f ? nhi : hi;
+        }
+        if (qr < q1) {
+          const bf16x8_t o8 = {to_bf16(lo[0]), to_bf16(lo[1]), to_bf16(lo[2]), to_bf16(lo[3]),
+                               to_bf16(hi[0]), to_bf16(hi[1]), to_bf16(hi[2]), to_bf16(hi[3])};
+          *(bf16x8_t*)(a.out + ((int64_t)qr * a.Hq + hr) * DH + 8 * cl) = o8;
+        }
+      }
+    }
+    if (qvalid && hg == 0) a.lse[(int64_t)qi * a.Hq + hq] = den > 0.f ? M + __logf(den) : -INFINITY;
   }
 }
 
@@ -811,7 +878,12 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
   if (blocks <= 0) return hipSuccess;
-  flash_dispatch_dh<false, 0, 0>(fa, s.dh, blocks, stream);
+  switch (s.top_k) {
+    case 1: flash_dispatch_dh<false, 0, 0>(fa, s.dh, blocks, stream); break;
+    case 2: flash_dispatch_dh<false, 1, 0>(fa, s.dh, blocks, stream); break;
+    case 3: flash_dispatch_dh<false, 2, 0>(fa, s.dh, blocks, stream); break;
+    default: flash_dispatch_dh<false, 3, 0>(fa, s.dh, blocks, stream); break;
+  }
   return hipGetLastError();
 }
 
