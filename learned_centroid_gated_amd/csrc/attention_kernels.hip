@@ -571,12 +571,13 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     }
 
     // ------------------------------------------------------------ online softmax
-    float tmax = -INFINITY;
+    // row maximum: four independent chains of 8 (v_max3 steps), then over the lane pair
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int vi = 0; vi < 16; ++vi) tmax = fmaxf(tmax, sacc[kb][vi]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+      for (int vi = 0; vi < 16; ++vi) mx[2 * kb + (vi >> 3)] = fmaxf(mx[2 * kb + (vi >> 3)], sacc[kb][vi]);
+    float tmax = pair32_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
     if constexpr (MKS > 0) tmax = tmax < kMaskFloor ? -INFINITY : tmax;
     tmax *= a.sl2;
     // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   // rows: in the accumulator layout one wave-wide access would touch 32 rows at 16 bytes each,
   // and the vector memory path spends a cycle per cache line touched. Lanes of rows without a
   // query stay active (shuffles and the window pass's barrier) but store nothing.
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
+  const float l_tot = pair32_sum(l_run);
   const float L_own = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   constexpr int RPI = 64 / CH;  // rows per transposed access (CH lanes per row)
   const int cl = l % CH;        // this lane's 16-byte chunk of the row in transposed accesses

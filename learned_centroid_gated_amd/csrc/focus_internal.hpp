@@ -28,6 +28,18 @@ __device__ __forceinline__ int shfl_xor_i(int x, int m) { return __shfl_xor(x, m
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum of x over the lane pair (l, l ^ 32) without a trip through LDS: gfx950's
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of its second,
+// so with both operands equal to x each lane ends up holding the pair's two values.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
