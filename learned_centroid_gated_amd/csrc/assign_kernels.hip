@@ -235,16 +235,24 @@ __global__ __launch_bounds__(256) void sinkhorn_rows_kernel(const float* __restr
       cs[4 * c + e] = 0.f;
     }
 
-  for (int64_t row = r_begin + wave * RPW + rg; row < r_end; row += 4 * RPW) {
-    float s[NC];
+  // the next row's scores are loaded while this row is reduced
+  auto load_row = [&](int64_t row, f32x4_t (&x)[CPL]) {
     const float* sp = S + row * ldS;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      int col = 4 * q + 4 * LPR * c;
-      f32x4_t x = col < K ? *(const f32x4_t*)(sp + col) : f32x4_t{};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * c + e] = x[e];
+      const int col = 4 * q + 4 * LPR * c;
+      x[c] = (row < r_end && col < K) ? *(const f32x4_t*)(sp + col) : f32x4_t{};
     }
+  };
+  f32x4_t nxt[CPL];
+  load_row(r_begin + wave * RPW + rg, nxt);
+  for (int64_t row = r_begin + wave * RPW + rg; row < r_end; row += 4 * RPW) {
+    float s[NC];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * c + e] = nxt[c][e];
+    load_row(row + 4 * RPW, nxt);
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NC; ++i)
@@ -344,14 +352,26 @@ static hipError_t sinkhorn_rows(const float* S, int64_t n, int K, int ldS, const
   return hipGetLastError();
 }
 
+// Lanes per row for K columns when every lane holds 16 of them (4 float4 chunks): the fewer
+// lanes a row takes, the more rows a wave reduces at once and the shorter the shuffle trees.
+int lanes_per_row(int K) {
+  int lpr = 1;
+  while (lpr < 64 && 16 * lpr < K) lpr *= 2;
+  return lpr;
+}
+
 hipError_t launch_sinkhorn_iter(const float* S, int64_t n, int K, int ldS, float* v,
                                 float2* partials, int nblocks, hipStream_t stream) {
   hipError_t e;
-  if (K <= 16) e = sinkhorn_rows<4, 1>(S, n, K, ldS, v, partials, nblocks, stream);
-  else if (K <= 64) e = sinkhorn_rows<16, 1>(S, n, K, ldS, v, partials, nblocks, stream);
-  else if (K <= 256) e = sinkhorn_rows<64, 1>(S, n, K, ldS, v, partials, nblocks, stream);
-  else if (K <= 512) e = sinkhorn_rows<64, 2>(S, n, K, ldS, v, partials, nblocks, stream);
-  else e = sinkhorn_rows<64, 4>(S, n, K, ldS, v, partials, nblocks, stream);
+  switch (lanes_per_row(K)) {
+    case 1: e = sinkhorn_rows<1, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+    case 2: e = sinkhorn_rows<2, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+    case 4: e = sinkhorn_rows<4, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+    case 8: e = sinkhorn_rows<8, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+    case 16: e = sinkhorn_rows<16, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+    case 32: e = sinkhorn_rows<32, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+    default: e = sinkhorn_rows<64, 4>(S, n, K, ldS, v, partials, nblocks, stream); break;
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sinkhorn_cols_kernel, dim3(K), dim3(256), 0, stream, partials, nblocks, K,
                      log((double)n / (double)K), v);
@@ -447,11 +467,15 @@ static hipError_t topk_launch(const float* S, const float* v, int64_t n, int K, 
 
 hipError_t launch_topk(const float* S, const float* v, int64_t n, int K, int ldS, int top_k,
                        int32_t* groups, hipStream_t stream) {
-  if (K <= 16) return topk_launch<4, 1>(S, v, n, K, ldS, top_k, groups, stream);
-  if (K <= 64) return topk_launch<16, 1>(S, v, n, K, ldS, top_k, groups, stream);
-  if (K <= 256) return topk_launch<64, 1>(S, v, n, K, ldS, top_k, groups, stream);
-  if (K <= 512) return topk_launch<64, 2>(S, v, n, K, ldS, top_k, groups, stream);
-  return topk_launch<64, 4>(S, v, n, K, ldS, top_k, groups, stream);
+  switch (lanes_per_row(K)) {
+    case 1: return topk_launch<1, 4>(S, v, n, K, ldS, top_k, groups, stream);
+    case 2: return topk_launch<2, 4>(S, v, n, K, ldS, top_k, groups, stream);
+    case 4: return topk_launch<4, 4>(S, v, n, K, ldS, top_k, groups, stream);
+    case 8: return topk_launch<8, 4>(S, v, n, K, ldS, top_k, groups, stream);
+    case 16: return topk_launch<16, 4>(S, v, n, K, ldS, top_k, groups, stream);
+    case 32: return topk_launch<32, 4>(S, v, n, K, ldS, top_k, groups, stream);
+    default: return topk_launch<64, 4>(S, v, n, K, ldS, top_k, groups, stream);
+  }
 }
 
 }  // namespace focus
