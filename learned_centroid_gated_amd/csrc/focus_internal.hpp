@@ -77,7 +77,7 @@ hipError_t launch_fill_f32(float* p, float value, int64_t count, hipStream_t str
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t count, hipStream_t stream);
 
 // Stable counting sort of memberships (bucket).
-constexpr int kBucketChunk = 256;
+constexpr int kBucketChunk = 64;  // tokens per chunk: one wave of the scatter pass, one step
 hipError_t launch_bucket(const int32_t* groups, int batch, int64_t n, int K, int top_k,
                          int32_t* offsets, int32_t* idx, int32_t* slot, int32_t* counts,
                          int32_t* totals, hipStream_t stream);
