@@ -22,8 +22,13 @@ namespace focus {
 //
 // Block tile 128 x (32*NT), k-chunks of 32: the chunk's fp32 tiles come from global memory into
 // registers one chunk ahead, are split, and are stored as three bf16 planes per operand in
-// LDS (rows padded to 80 bytes: 16 lanes reading 16 bytes of 16 consecutive rows hit 16
-// distinct bank quads). Each wave owns 32 rows and NT 32x32 accumulator tiles.
+// LDS. A plane row holds the chunk's 32 values in four 16-byte quarters, quarter q of row r
+// stored at position q ^ ((r / 4) % 4): 16 lanes reading one quarter of 16 consecutive rows
+// (an MFMA operand) hit 16 distinct bank quads, and 8-byte writes of 8 whole rows cover every
+// bank exactly twice. Each wave owns 32 rows and NT 32x32 accumulator tiles.
+__device__ __forceinline__ int plane_at(int r, int c) {  // bf16 index of row r, column c < 32
+  return r * 32 + (((c >> 3) ^ ((r >> 2) & 3)) << 3) + (c & 7);
+}
 struct Bf16x4Planes {
   bf16x4_t h, m, l;
 };
@@ -43,13 +48,13 @@ __device__ __forceinline__ Bf16x4Planes split3(f32x4_t x) {
 }
 
 template <int NT>
-__global__ __launch_bounds__(256) void gemm_nt_split_kernel(const float* __restrict__ A,
+__global__ __launch_bounds__(256, 3) void gemm_nt_split_kernel(const float* __restrict__ A,
                                                             const float* __restrict__ B,
                                                             float* __restrict__ C, int64_t M,
                                                             int N, int Kd, int ldc) {
-  constexpr int BM = 128, BN = 32 * NT, BK = 32, LDA = 40;  // LDA: bf16 per padded row
-  __shared__ __attribute__((aligned(16))) __bf16 As[3][BM * LDA];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[3][BN * LDA];
+  constexpr int BM = 128, BN = 32 * NT, BK = 32;
+  __shared__ __attribute__((aligned(16))) __bf16 As[3][BM * BK];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[3][BN * BK];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, j = l & 31, g = l >> 5;
   const int64_t m0 = (int64_t)blockIdx.x * BM;
   const int n0 = blockIdx.y * BN;
@@ -81,17 +86,19 @@ __global__ __launch_bounds__(256) void gemm_nt_split_kernel(const float* __restr
     for (int i = 0; i < 4; ++i) {
       int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
       const Bf16x4Planes pl = split3(ra[i]);
-      *(bf16x4_t*)&As[0][r * LDA + c] = pl.h;
-      *(bf16x4_t*)&As[1][r * LDA + c] = pl.m;
-      *(bf16x4_t*)&As[2][r * LDA + c] = pl.l;
+      const int o = plane_at(r, c);
+      *(bf16x4_t*)&As[0][o] = pl.h;
+      *(bf16x4_t*)&As[1][o] = pl.m;
+      *(bf16x4_t*)&As[2][o] = pl.l;
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
       const Bf16x4Planes pl = split3(rb[i]);
-      *(bf16x4_t*)&Bs[0][r * LDA + c] = pl.h;
-      *(bf16x4_t*)&Bs[1][r * LDA + c] = pl.m;
-      *(bf16x4_t*)&Bs[2][r * LDA + c] = pl.l;
+      const int o = plane_at(r, c);
+      *(bf16x4_t*)&Bs[0][o] = pl.h;
+      *(bf16x4_t*)&Bs[1][o] = pl.m;
+      *(bf16x4_t*)&Bs[2][o] = pl.l;
     }
     __syncthreads();
     if (k0 + BK < Kd) load(k0 + BK);
@@ -101,13 +108,13 @@ __global__ __launch_bounds__(256) void gemm_nt_split_kernel(const float* __restr
       bf16x8_t a[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-        a[p] = *(const bf16x8_t*)&As[p][(wave * 32 + j) * LDA + ks * 16 + 8 * g];
+        a[p] = *(const bf16x8_t*)&As[p][plane_at(wave * 32 + j, ks * 16 + 8 * g)];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         bf16x8_t b[3];
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          b[p] = *(const bf16x8_t*)&Bs[p][(t * 32 + j) * LDA + ks * 16 + 8 * g];
+          b[p] = *(const bf16x8_t*)&Bs[p][plane_at(t * 32 + j, ks * 16 + 8 * g)];
         // small terms first
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], acc[t], 0, 0, 0);
