@@ -559,10 +559,8 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int d = qi - (ks + kk0 + e);
-              ok[e] = d >= 0 && d < window;
-            }
+            for (int e = 0; e < 4; ++e)  // 0 <= d < window as one unsigned compare
+              ok[e] = (uint32_t)(qi - (ks + kk0 + e)) < (uint32_t)window;
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
