@@ -391,7 +391,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the Focus path here runs on a single MI355X and has no "
-              "multi-GPU mode (see the sharding design in DESIGN.md); run with --gpus 1.",
+              "multi-GPU mode (no collectives or sharding are built); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"

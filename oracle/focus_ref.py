@@ -12,7 +12,7 @@ Pages cited (all describe the method "Focus", arXiv 2604.03260):
         grouping), 2.1.2 (gated attention, with its gate formula), 2.1.3 (top-k inference).
   (DE)  flowki-club.de blog post on Focus, section "Wie Focus funktioniert".
 
-What the pages fix, and the reading taken where they are silent (each is listed in the design doc):
+What the pages fix, and the reading taken where they are silent:
   * Scores: hidden states are projected into a d_g-dimensional group space and compared
     with K centroids C in R^{K x d_g} (ZH 2.1.1; NL Kerncomponenten 1). Reading: plain
     dot product S = (H W_g) C^T, no bias, norm or temperature; one W_g per layer shared
