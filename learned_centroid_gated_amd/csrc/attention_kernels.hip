@@ -41,48 +41,39 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(const i32x4_t* __restric
                                                         i32x4_t* __restrict__ kg,
                                                         i32x4_t* __restrict__ vg,
                                                         i32x4_t* __restrict__ kinfo) {
+  // A block copies 4 slots at a time (slot indices uniform: their tokens come from scalar
+  // loads); thread t moves 16-byte chunk t (+256, ...) of each of the 4 rows, K chunks first.
+  constexpr int SPB = 4;
   const int per = 2 * ckv;  // 16-byte chunks per slot
-  const int64_t total = nk * per;
-  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
-  for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
-    i32x4_t val[4];
-    int64_t dst[4];
-    int which[4];
+  const int t = threadIdx.x;
+  for (int64_t s0 = (int64_t)blockIdx.x * SPB; s0 < nk; s0 += (int64_t)gridDim.x * SPB) {
+    int32_t tok[SPB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int64_t e = base + u * 256;
-      which[u] = -1;
-      if (e >= total) continue;
-      int64_t s = e / per;
-      int c = (int)(e - s * per);
-      int32_t tok = idx[s];
-      if (tok < 0) continue;
-      if (c == 0) {
-        // the membership's rank r among the token's ascending groups: lower groups come first
-        i32x4_t info = {tok, -1, -1, -1};
-        for (int r = 0; r < top_k; ++r) {
-          if (slot[(int64_t)tok * top_k + r] == (int32_t)s) {
-            for (int c2 = 0; c2 < r && c2 < 3; ++c2) info[1 + c2] = groups[(int64_t)tok * top_k + c2];
-            break;
-          }
+    for (int j = 0; j < SPB; ++j) tok[j] = s0 + j < nk ? idx[s0 + j] : -1;
+    if (t < SPB && tok[t] >= 0) {
+      // the membership's rank r among the token's ascending groups: lower groups come first
+      const int64_t s = s0 + t;
+      i32x4_t info = {tok[t], -1, -1, -1};
+      for (int r = 0; r < top_k; ++r) {
+        if (slot[(int64_t)tok[t] * top_k + r] == (int32_t)s) {
+          for (int c2 = 0; c2 < r && c2 < 3; ++c2) info[1 + c2] = groups[(int64_t)tok[t] * top_k + c2];
+          break;
         }
-        kinfo[s] = info;
       }
-      if (c < ckv) {
-        val[u] = k[(int64_t)tok * ckv + c];
-        dst[u] = s * ckv + c;
-        which[u] = 0;
-      } else {
-        c -= ckv;
-        val[u] = v[(int64_t)tok * ckv + c];
-        dst[u] = s * ckv + c;
-        which[u] = 1;
-      }
+      kinfo[s] = info;
     }
+    for (int c = t; c < per; c += 256) {
+      const bool isk = c < ckv;
+      const int cc = isk ? c : c - ckv;
+      const i32x4_t* src = isk ? k : v;
+      i32x4_t* dst = isk ? kg : vg;
+      i32x4_t val[SPB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (which[u] == 0) kg[dst[u]] = val[u];
-      else if (which[u] == 1) vg[dst[u]] = val[u];
+      for (int j = 0; j < SPB; ++j)
+        if (tok[j] >= 0) val[j] = src[(int64_t)tok[j] * ckv + cc];
+#pragma unroll
+      for (int j = 0; j < SPB; ++j)
+        if (tok[j] >= 0) dst[(s0 + j) * ckv + cc] = val[j];
     }
   }
 }
@@ -91,8 +82,7 @@ hipError_t launch_gather_kv(const uint16_t* k, const uint16_t* v, const int32_t*
                             const int32_t* groups, const int32_t* slot, const AttnShape& s,
                             uint16_t* kg, uint16_t* vg, int32_t* kinfo, hipStream_t stream) {
   const int ckv = s.Hkv * s.dh / 8;
-  int64_t total = s.nk * 2 * ckv;
-  int64_t blocks = (total + 1023) / 1024;
+  int64_t blocks = (s.nk + 3) / 4;  // 4 slots per block
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(gather_kv_kernel, dim3(blocks), dim3(256), 0, stream, (const i32x4_t*)k,
