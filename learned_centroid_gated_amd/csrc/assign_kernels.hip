@@ -6,6 +6,8 @@
 // gist.science/zh, section 2.1.1: projection into centroid space, similarity to K centroids,
 // Sinkhorn in place of softmax so each group gets equal token mass; section 2.1.3: each token
 // joins its k highest-scoring groups at inference).
+#include <type_traits>
+
 #include "focus_internal.hpp"
 
 namespace focus {
@@ -151,6 +153,177 @@ hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int64_t 
   } else {
     hipLaunchKernelGGL(gemm_nt_split_kernel<4>, dim3(mb, (N + 127) / 128), block, 0, stream, A, B,
                        C, M, N, Kd, ldc);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- planes GEMM
+// The same product when B has been split once into its planes (Bp[3][N][Kd], bf16): instead of
+// every block loading and splitting the shared B tile for every k-chunk, the chunk's planes go
+// from memory straight into LDS (global_load_lds, per-lane offsets that apply the quarter
+// permutation) into a double buffer, one chunk ahead of the MFMAs that read them.
+__global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ B,
+                                                           int64_t count, __bf16* __restrict__ P) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < count;
+       i += (int64_t)gridDim.x * 256 * 4) {
+    if (i + 4 <= count) {
+      const Bf16x4Planes pl = split3(*(const f32x4_t*)(B + i));
+      *(bf16x4_t*)(P + i) = pl.h;
+      *(bf16x4_t*)(P + count + i) = pl.m;
+      *(bf16x4_t*)(P + 2 * count + i) = pl.l;
+    } else {
+      for (int64_t j = i; j < count; ++j) {
+        const __bf16 h = (__bf16)B[j];
+        const float r1 = B[j] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        P[j] = h;
+        P[count + j] = m;
+        P[2 * count + j] = (__bf16)(r1 - (float)m);
+      }
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256, 2) void gemm_nt_planes_kernel(const float* __restrict__ A,
+                                                                const __bf16* __restrict__ Bp,
+                                                                float* __restrict__ C, int64_t M,
+                                                                int N, int Kd, int ldc) {
+  constexpr int BM = 128, BN = 32 * NT, BK = 32;
+  constexpr int BTILE = 3 * BN * BK;             // bf16 per B tile (three planes)
+  constexpr int BINSTS = BTILE * 2 / 1024;       // 1 KB copies per B tile
+  constexpr int BPW = (BINSTS + 3) / 4;          // per wave
+  __shared__ __attribute__((aligned(1024))) __bf16 As[3][BM * BK];
+  __shared__ __attribute__((aligned(1024))) __bf16 Bs[2][BTILE];
+  const int tid = threadIdx.x, l = tid & 63, j = l & 31, g = l >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+
+  // copy ii of a B tile fills rows 16 (ii % (BN / 16)) .. + 15 of plane ii / (BN / 16); lane L
+  // lands at row + L / 4, physical quarter L % 4, which holds logical quarter
+  // (L % 4) ^ ((row / 4) % 4). Rows past N re-read row N - 1 (their columns are never stored).
+  uint32_t boff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int ii = wave + 4 * i;
+    const int pl = ii / (BN / 16), rb = ii % (BN / 16);
+    const int r = rb * 16 + l / 4;
+    const int q = (l % 4) ^ ((r >> 2) & 3);
+    const int row = min(n0 + r, N - 1);
+    boff[i] = (uint32_t)((((int64_t)pl * N + row) * Kd + 8 * q) * 2);
+  }
+  auto copy_b = [&](int k0, __bf16* dst) __attribute__((always_inline)) {
+    const char* base = (const char*)(Bp + k0);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int ii = wave + 4 * i;
+      if (ii < BINSTS) dma16(base, boff[i], (char*)dst + ii * 1024);
+    }
+  };
+  auto lds_barrier = []() __attribute__((always_inline)) {  // LDS only: copies stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16_t{};
+
+  f32x4_t ra[4];
+  auto load_a = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
+      int64_t gr = m0 + r;
+      ra[i] = gr < M ? *(const f32x4_t*)(A + gr * Kd + k0 + c) : f32x4_t{};
+    }
+  };
+
+  // one k-chunk; the loop is unrolled by two so each B buffer is a fixed LDS address
+  auto chunk = [&](int k0, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;  // B buffer of this chunk
+    lds_barrier();  // every wave is done with As and with the other B buffer
+    // The wait for ra below (vmcnt(0): these are the newest loads) also covers this chunk's B
+    // copies, which went out before them.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid + 256 * i, r = e >> 3, c = (e & 7) * 4;
+      const Bf16x4Planes pl = split3(ra[i]);
+      const int o = plane_at(r, c);
+      *(bf16x4_t*)&As[0][o] = pl.h;
+      *(bf16x4_t*)&As[1][o] = pl.m;
+      *(bf16x4_t*)&As[2][o] = pl.l;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (k0 + BK < Kd) {
+      copy_b(k0 + BK, Bs[P ^ 1]);
+      load_a(k0 + BK);
+    }
+    lds_barrier();  // As and this chunk's B planes are in LDS
+    const __bf16* bsb = Bs[P];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t a[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        a[p] = *(const bf16x8_t*)&As[p][plane_at(wave * 32 + j, ks * 16 + 8 * g)];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bf16x8_t b[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          b[p] = *(const bf16x8_t*)&bsb[p * BN * BK + plane_at(t * 32 + j, ks * 16 + 8 * g)];
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc[t], 0, 0, 0);
+      }
+    }
+  };
+  copy_b(0, Bs[0]);
+  load_a(0);
+  for (int k0 = 0; k0 < Kd; k0 += 2 * BK) {
+    chunk(k0, std::integral_constant<int, 0>{});
+    if (k0 + BK < Kd) chunk(k0 + BK, std::integral_constant<int, 1>{});
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int col = n0 + t * 32 + j;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int64_t row = m0 + wave * 32 + (v >> 2) * 8 + 4 * g + (v & 3);
+      if (row < M && col < N) C[row * ldc + col] = acc[t][v];
+    }
+  }
+}
+
+hipError_t launch_split_planes(const float* B, int64_t count, __bf16* P, hipStream_t stream) {
+  int64_t blocks = (count + 1023) / 1024;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(split_planes_kernel, dim3(blocks), dim3(256), 0, stream, B, count, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt_f32_planes(const float* A, const __bf16* Bp, float* C, int64_t M, int N,
+                                     int Kd, int ldc, hipStream_t stream) {
+  if (Kd % 32 != 0) return hipErrorInvalidValue;
+  dim3 block(256);
+  int64_t mb = (M + 127) / 128;
+  if (N <= 32) {
+    hipLaunchKernelGGL(gemm_nt_planes_kernel<1>, dim3(mb, (N + 31) / 32), block, 0, stream, A, Bp,
+                       C, M, N, Kd, ldc);
+  } else if (N <= 64) {
+    hipLaunchKernelGGL(gemm_nt_planes_kernel<2>, dim3(mb, (N + 63) / 64), block, 0, stream, A, Bp,
+                       C, M, N, Kd, ldc);
+  } else {
+    hipLaunchKernelGGL(gemm_nt_planes_kernel<4>, dim3(mb, (N + 127) / 128), block, 0, stream, A,
+                       Bp, C, M, N, Kd, ldc);
   }
   return hipGetLastError();
 }

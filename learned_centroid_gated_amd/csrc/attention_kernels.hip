@@ -223,26 +223,6 @@ struct FlashSmem {
 // Tile classes seen by one wave.
 enum { kSkip = 0, kEdge = 1, kFar = 2, kFull = 3 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-// One wave-wide global_load_lds_dwordx4: lane L copies 16 bytes from base + voff (base uniform,
-// voff per lane) to LDS byte lds_dst + 16 L. Issued through inline asm so the compiler does not
-// treat the copy as a pending write to every LDS location: with the builtin it waits for the
-// whole copy before the first LDS read that follows, which serialises the prefetch of the next
-// tile with the compute on the current one. The caller waits (vmcnt) before the data is read.
-// The LDS destination goes in as a pointer operand (not an integer), so the compiler keeps
-// treating the buffer as written by the asm statement.
-__device__ __forceinline__ void dma16(const char* base, uint32_t voff, void* lds_dst) {
-  lds_char_t* m = (lds_char_t*)lds_dst;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory");
-}
-
-// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt at their maxima)
-constexpr int kWaitVmcnt0 = 0x0F70;
 
 constexpr float kMaskBias = -0x1p100f;   // ownership bias of an excluded pair (before scaling)
 constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully masked rows

@@ -3,6 +3,8 @@
 // host without a GPU; no HIP call is made on an error path.
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/focus.h"
 #include "focus_internal.hpp"
 
@@ -46,6 +48,7 @@ struct AssignWs {
   float* S;
   float* Z;
   float* Bt;
+  __bf16* Bp;  // bf16 planes of the current product's B operand (3 x its size)
   float* v;
   float2* partials;
 };
@@ -57,6 +60,8 @@ size_t assign_carve(void* ws, int64_t n, int d, int d_g, int K, AssignWs* out) {
   w.S = c.take<float>((size_t)n * padded_k(K));
   w.Z = fold ? nullptr : c.take<float>((size_t)n * d_g);
   w.Bt = c.take<float>((size_t)(fold ? K : d_g) * d);
+  const size_t bmax = fold ? (size_t)K * d : std::max((size_t)d_g * d, (size_t)K * d_g);
+  w.Bp = c.take<__bf16>(3 * bmax);
   w.v = c.take<float>((size_t)padded_k(K));
   w.partials = c.take<float2>((size_t)sinkhorn_blocks(n, K) * K);
   if (out) *out = w;
@@ -156,15 +161,24 @@ int focus_assign(const float* hidden, const float* w_g, const float* centroids, 
   hipStream_t st = (hipStream_t)stream;
   const int ldS = padded_k(K);
   hipError_t e;
+  // the n-row products take their small operand as bf16 planes split once per call (needs the
+  // inner dimension to be a multiple of 32), else split on the fly
+  auto product = [&](const float* a, const float* b, float* c, int64_t m, int nn, int kd,
+                     int ldc) -> hipError_t {
+    if (kd % 32 != 0) return launch_gemm_nt_f32(a, b, c, m, nn, kd, ldc, st);
+    hipError_t e2 = launch_split_planes(b, (int64_t)nn * kd, w.Bp, st);
+    if (e2 != hipSuccess) return e2;
+    return launch_gemm_nt_f32_planes(a, w.Bp, c, m, nn, kd, ldc, st);
+  };
   if (assign_folds(d, d_g, K)) {
     // Bt = (W_g C^T)^T = C W_g^T  [K, d];  S = H Bt^T
     e = launch_gemm_nt_f32(centroids, w_g, w.Bt, K, d, d_g, d, st);
-    if (e == hipSuccess) e = launch_gemm_nt_f32(hidden, w.Bt, w.S, n, K, d, ldS, st);
+    if (e == hipSuccess) e = product(hidden, w.Bt, w.S, n, K, d, ldS);
   } else {
     // Bt = W_g^T [d_g, d];  Z = H W_g;  S = Z C^T
     e = launch_transpose_f32(w_g, w.Bt, d, d_g, st);
-    if (e == hipSuccess) e = launch_gemm_nt_f32(hidden, w.Bt, w.Z, n, d_g, d, d_g, st);
-    if (e == hipSuccess) e = launch_gemm_nt_f32(w.Z, centroids, w.S, n, K, d_g, ldS, st);
+    if (e == hipSuccess) e = product(hidden, w.Bt, w.Z, n, d_g, d, d_g);
+    if (e == hipSuccess) e = product(w.Z, centroids, w.S, n, K, d_g, ldS);
   }
   if (e == hipSuccess) e = launch_fill_f32(w.v, 0.f, K, st);
   const int nblk = sinkhorn_blocks(n, K);

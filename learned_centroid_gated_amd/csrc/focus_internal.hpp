@@ -58,12 +58,42 @@ inline int64_t xcd_grid(int64_t total) {
   return per * kXcds;
 }
 
+// ------------------------------------------------------------------ LDS copies
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// One wave-wide global_load_lds_dwordx4: lane L copies 16 bytes from base + voff (base uniform,
+// voff per lane) to LDS byte lds_dst + 16 L. Issued through inline asm so the compiler does not
+// treat the copy as a pending write to every LDS location: with the builtin it waits for the
+// whole copy before the first LDS read that follows, which serialises the prefetch of the next
+// tile with the compute on the current one. The caller waits (vmcnt) before the data is read.
+// The LDS destination goes in as a pointer operand (not an integer), so the compiler keeps
+// treating the buffer as written by the asm statement.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, void* lds_dst) {
+  lds_char_t* m = (lds_char_t*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory");
+}
+
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------------------ launchers
 // All launchers enqueue on `stream` and return hipSuccess or the launch error.
 
-// C[M, ldc] (first N columns) = A[M, Kd] * B[N, Kd]^T, fp32 in and out, fp32 MFMA.
+// C[M, ldc] (first N columns) = A[M, Kd] * B[N, Kd]^T, fp32 in and out, to fp32 accuracy on the
+// bf16 MFMA (each operand split into three bf16 parts on the fly).
 hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int64_t M, int N, int Kd,
                               int ldc, hipStream_t stream);
+// The same product with B given as its three bf16 planes Bp[3][N][Kd] (split_planes below);
+// requires Kd % 32 == 0. Bp must stay valid until the product has run.
+hipError_t launch_gemm_nt_f32_planes(const float* A, const __bf16* Bp, float* C, int64_t M, int N,
+                                     int Kd, int ldc, hipStream_t stream);
+// P[p * count + i] = part p (0: bf16(x), 1: bf16 of the remainder, 2: bf16 of what is left) of
+// x = B[i], for i < count.
+hipError_t launch_split_planes(const float* B, int64_t count, __bf16* P, hipStream_t stream);
 // Bt[N, Kd] = transpose of B[Kd, N], fp32.
 hipError_t launch_transpose_f32(const float* B, float* Bt, int Kd, int N, hipStream_t stream);
 // One Sinkhorn iteration on S [n, ldS] (first K columns): row step with the current v,
