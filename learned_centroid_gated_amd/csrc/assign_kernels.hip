@@ -586,61 +586,73 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S,
       colx[4 * c + e] = col < K ? col : kNone;
       vv[4 * c + e] = col < K ? v[col] : 0.f;
     }
-  const int64_t rows_per_block = 4 * RPW;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_block + wave * RPW + rg;
-  if (row >= n) return;  // a whole row group leaves together; shuffles stay within it
-  float b[NC];
-  const float* sp = S + row * ldS;
+  // the block's waves walk row groups grid-stride, each loading its next row group while it
+  // selects from the current one (a row group leaves the loop together: shuffles stay inside)
+  const int64_t step = (int64_t)gridDim.x * 4 * RPW;
+  f32x4_t nx[CPL];
+  auto load_row = [&](int64_t row) {
+    const float* sp = S + row * ldS;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    int col = 4 * q + 4 * LPR * c;
-    f32x4_t x = col < K ? *(const f32x4_t*)(sp + col) : f32x4_t{};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) b[4 * c + e] = x[e] + vv[4 * c + e];
-  }
-  unsigned taken = 0;
-  int sel[8];
-  for (int r = 0; r < top_k; ++r) {
-    float bv = 0.f;
-    int bi = kNone;
-#pragma unroll
-    for (int i = 0; i < NC; ++i)
-      if (!((taken >> i) & 1u) && better(b[i], colx[i], bv, bi)) {
-        bv = b[i];
-        bi = colx[i];
-      }
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) {
-      float v2 = shfl_xor_f(bv, o);
-      int i2 = shfl_xor_i(bi, o);
-      if (better(v2, i2, bv, bi)) {
-        bv = v2;
-        bi = i2;
-      }
+    for (int c = 0; c < CPL; ++c) {
+      const int col = 4 * q + 4 * LPR * c;
+      nx[c] = (row < n && col < K) ? *(const f32x4_t*)(sp + col) : f32x4_t{};
     }
-    sel[r] = bi;
+  };
+  int64_t row = (int64_t)blockIdx.x * 4 * RPW + wave * RPW + rg;
+  load_row(row);
+  for (; row < n; row += step) {
+    float b[NC];
 #pragma unroll
-    for (int i = 0; i < NC; ++i)
-      if (colx[i] == bi) taken |= 1u << i;
-  }
-  // ascending order of the selected set
-  for (int a = 1; a < top_k; ++a) {
-    int x = sel[a], p = a - 1;
-    while (p >= 0 && sel[p] > x) {
-      sel[p + 1] = sel[p];
-      --p;
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[4 * c + e] = nx[c][e] + vv[4 * c + e];
+    load_row(row + step);
+    unsigned taken = 0;
+    int sel[8];
+    for (int r = 0; r < top_k; ++r) {
+      float bv = 0.f;
+      int bi = kNone;
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        if (!((taken >> i) & 1u) && better(b[i], colx[i], bv, bi)) {
+          bv = b[i];
+          bi = colx[i];
+        }
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) {
+        float v2 = shfl_xor_f(bv, o);
+        int i2 = shfl_xor_i(bi, o);
+        if (better(v2, i2, bv, bi)) {
+          bv = v2;
+          bi = i2;
+        }
+      }
+      sel[r] = bi;
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        if (colx[i] == bi) taken |= 1u << i;
     }
-    sel[p + 1] = x;
+    // ascending order of the selected set
+    for (int a = 1; a < top_k; ++a) {
+      int x = sel[a], p = a - 1;
+      while (p >= 0 && sel[p] > x) {
+        sel[p + 1] = sel[p];
+        --p;
+      }
+      sel[p + 1] = x;
+    }
+    if (q == 0)
+      for (int r = 0; r < top_k; ++r) groups[row * top_k + r] = sel[r];
   }
-  if (q == 0)
-    for (int r = 0; r < top_k; ++r) groups[row * top_k + r] = sel[r];
 }
 
 template <int LPR, int CPL>
 static hipError_t topk_launch(const float* S, const float* v, int64_t n, int K, int ldS, int top_k,
                               int32_t* groups, hipStream_t stream) {
-  int64_t rpb = 4 * (kWave / LPR);
-  hipLaunchKernelGGL((topk_kernel<LPR, CPL>), dim3((n + rpb - 1) / rpb), dim3(256), 0, stream, S, v,
+  const int64_t rpb = 4 * (kWave / LPR);
+  int64_t blocks = (n + rpb - 1) / rpb;
+  if (blocks > 8192) blocks = 8192;  // beyond that the blocks walk further row groups
+  hipLaunchKernelGGL((topk_kernel<LPR, CPL>), dim3(blocks), dim3(256), 0, stream, S, v,
                      n, K, ldS, top_k, groups);
   return hipGetLastError();
 }
