@@ -299,6 +299,16 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     qpos = qi;
   }
 
+  // window pass: the token's membership slots load with the query row, their group LSEs with
+  // the first tile, so the merge epilogue starts with both in registers
+  constexpr int TK = NLOW + 1;
+  int srow[GROUP ? 1 : TK];
+  float Lr[GROUP ? 1 : TK];
+  if constexpr (!GROUP) {
+#pragma unroll
+    for (int r = 0; r < TK; ++r) srow[r] = qvalid ? a.slot[(int64_t)qi * TK + r] : -1;
+  }
+
   bf16x8_t qreg[NS];
   {
     const int qrow = qvalid ? (GROUP ? qpos : qi) : 0;
@@ -598,7 +608,11 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
   // group pass: the first tile's copies go out with the query-row loads and one wait covers
   // both (measured neutral to slightly worse for the window pass, which keeps two waits)
-  if constexpr (!GROUP) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (!GROUP) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+    for (int r = 0; r < TK; ++r) Lr[r] = srow[r] >= 0 ? a.lseg[(int64_t)srow[r] * a.Hq + hq] : -INFINITY;
+  }
   if (ntiles > 0) issue_tile(kv_lo, smem[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (MKS > 0) {
@@ -672,17 +686,9 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   } else {
     // merge the window part with this token's group parts by log-sum-exp, in token order;
     // NLOW + 1 = top_k group parts per token
-    constexpr int TK = NLOW + 1;
-    float Lr[TK];
-    int srow[TK];
     float M = L_own;
 #pragma unroll
-    for (int r = 0; r < TK; ++r) {
-      const int sl = qvalid ? a.slot[(int64_t)qi * TK + r] : -1;
-      srow[r] = sl;
-      Lr[r] = sl >= 0 ? a.lseg[(int64_t)sl * a.Hq + hq] : -INFINITY;
-      M = fmaxf(M, Lr[r]);
-    }
+    for (int r = 0; r < TK; ++r) M = fmaxf(M, Lr[r]);
     float w_own = 0.f, den = 0.f, cr[TK];
 #pragma unroll
     for (int r = 0; r < TK; ++r) cr[r] = 0.f;

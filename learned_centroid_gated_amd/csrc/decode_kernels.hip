@@ -145,11 +145,28 @@ struct DecodeArgs {
   float* part_ml;  // [B, Hq, splits, 2] (running max in log2 units, sum)
 };
 
+// x plus lane (l ^ 1), (l ^ 2), then the mirrored lane of the 8-lane half row and, for W = 16,
+// of the 16-lane row: data-parallel-primitive moves on the VALU, with no LDS round trip.
+// bound_ctrl makes every lane a valid source.
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                   CTRL, 0xF, 0xF, false));
+}
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {  // sum over the lane's aligned W-lane group
-#pragma unroll
-  for (int o = W / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  static_assert(W == 8 || W == 16, "lane groups of 8 or 16");
+  x = dpp_plus<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_plus<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_plus<0x141>(x);  // row_half_mirror
+  if constexpr (W == 16) x = dpp_plus<0x140>(x);  // row_mirror
   return x;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // The sequence's resolved key list is cut into `splits` contiguous pieces per (sequence, group
@@ -185,17 +202,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const int64_t v1 = v0 + per < total ? v0 + per : total;
   const int32_t* lst = a.list + (int64_t)b * a.per_seq;
 
-  // this lane's slice of the query heads, pre-scaled to log2 units
-  float qf[HD][8];
+  // this lane's slice of the query heads as bf16 pairs; scores are scaled after the reduction
+  i32x4_t qr[HD];
 #pragma unroll
   for (int hh = 0; hh < HD; ++hh) {
     const int hq = hq0 + (hh < nh ? hh : 0);
-    const i32x4_t raw = *(const i32x4_t*)(a.q + ((int64_t)b * a.Hq + hq) * DH + c * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[hh][2 * e] = __uint_as_float((uint32_t)raw[e] << 16) * a.sl2;
-      qf[hh][2 * e + 1] = __uint_as_float((uint32_t)raw[e] & 0xffff0000u) * a.sl2;
-    }
+    qr[hh] = *(const i32x4_t*)(a.q + ((int64_t)b * a.Hq + hq) * DH + c * 8);
   }
   float m_run[HD], l_run[HD], o[HD][8];
 #pragma unroll
@@ -235,21 +247,21 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (pk[u] < 0) continue;  // uniform within the lane group
-      float kf[8], vf[8];
+      float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float((uint32_t)kr[u][e] << 16);
-        kf[2 * e + 1] = __uint_as_float((uint32_t)kr[u][e] & 0xffff0000u);
         vf[2 * e] = __uint_as_float((uint32_t)vr[u][e] << 16);
         vf[2 * e + 1] = __uint_as_float((uint32_t)vr[u][e] & 0xffff0000u);
       }
 #pragma unroll
       for (int hh = 0; hh < HD; ++hh) {
         if (hh >= nh) break;
-        float sdot = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(qf[hh][e], kf[e], sdot);
-        sdot = group_sum<CHK>(sdot);
+        // bf16 products are exact in fp32; two chains of two pairs each
+        const float d0 = dot2_bf16((uint32_t)qr[hh][1], (uint32_t)kr[u][1],
+                                   dot2_bf16((uint32_t)qr[hh][0], (uint32_t)kr[u][0], 0.f));
+        const float d1 = dot2_bf16((uint32_t)qr[hh][3], (uint32_t)kr[u][3],
+                                   dot2_bf16((uint32_t)qr[hh][2], (uint32_t)kr[u][2], 0.f));
+        const float sdot = group_sum<CHK>(d0 + d1) * a.sl2;
         // lazy running max: rescale only when the score passes the reference by 2^8
         if (sdot > m_run[hh] + 8.f) {
           const float alpha = m_run[hh] == -INFINITY ? 0.f : fast_exp2(m_run[hh] - sdot);
