@@ -7,25 +7,25 @@
 // sees itself), then for each query group g_r the segment members at positions <= p - w'
 // whose lowest group shared with the query is g_r, so every allowed key appears once.
 //
-// The list is cut into `splits` contiguous pieces per (sequence, group of up to 4 query heads
-// of one kv head). A 256-thread block first resolves 256 list entries into key positions in
-// LDS (one per thread, dropping group members owned by a lower shared group), then every
-// 16-lane group takes one key at a time: each lane holds 8 dims of the query heads in
-// registers and reads one coalesced 16-byte chunk of the key's K and V rows, the dot products
-// are reduced across the 16 lanes, and a running (max, sum, O) per head absorbs the key. The
-// 16 lane groups' states are merged through LDS into one partial per block, and a second
-// kernel merges the partials by their log-sum-exp. The path is HBM-bound: every allowed key
-// costs one K row and one V row of the kv head.
+// Three steps. A plan kernel finds, per sequence, the window and each query group's slice of
+// its bucketed memberships; a list kernel resolves the virtual list into key positions once per
+// sequence (-1 for members that a lower shared group owns). The partial kernel cuts each list
+// into `splits` pieces; its blocks read every listed key's K and V rows, all kv heads of a
+// token at once where the head count allows, and keep a running (max, sum, O) per query head.
+// A combine kernel merges the pieces by log-sum-exp. The path is HBM-bound: every allowed key
+// costs one K row and one V row per kv head.
 #include "focus_internal.hpp"
 
 namespace focus {
 
 constexpr int kDecHeads = 4;     // query heads per block
 constexpr int kDecInfo = 12;     // per-sequence plan: lo, nl, -, then (segment start, count) x 4
+constexpr int kDecSplits = 16;   // key-list pieces per (sequence, head group)
+constexpr int kListBlocks = 32;  // list-resolution blocks per sequence (grid-stride over the list)
 
 int decode_splits(const DecodeShape& s) {
   (void)s;
-  return 16;
+  return kDecSplits;
 }
 
 // ============================================================================ plan
@@ -94,40 +94,40 @@ __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restr
                                                           int64_t Lmax, int K, int top_k,
                                                           int64_t per_seq,
                                                           int32_t* __restrict__ list) {
-  const int64_t chunks = (per_seq + 255) / 256;
-  const int b = (int)(blockIdx.x / chunks);
-  const int64_t vi = (blockIdx.x % chunks) * 256 + threadIdx.x;
+  const int b = (int)(blockIdx.x / kListBlocks);
   const int32_t* inf = info + (int64_t)b * kDecInfo;
   const int64_t lo = inf[0], nl = inf[1];
   int64_t total = nl;
   for (int r = 0; r < top_k; ++r) total += inf[4 + 2 * r];
-  if (vi >= total) return;
-  int pos = -1;
-  if (vi < nl) {
-    pos = (int)(lo + vi);
-  } else {
-    int qg[4];
-    for (int r = 0; r < top_k; ++r) qg[r] = q_groups[(int64_t)b * top_k + r];
-    int64_t rem = vi - nl;
-    for (int r = 0; r < top_k; ++r) {
-      const int64_t cnt = inf[4 + 2 * r];
-      if (rem < cnt) {
-        const int cand = cache_idx[(int64_t)b * Lmax * top_k + inf[3 + 2 * r] + rem];
-        // owned by g_r unless the key also holds a lower query group
-        bool owned = true;
-        const int32_t* kg = cache_groups + ((int64_t)b * Lmax + cand) * top_k;
-        for (int r2 = 0; r2 < top_k; ++r2) {
-          const int g2 = qg[r2];
-          if (g2 >= 0 && g2 < K && g2 < qg[r])
-            for (int r3 = 0; r3 < top_k; ++r3) owned = owned && kg[r3] != g2;
+  for (int64_t vi = (blockIdx.x % kListBlocks) * 256 + threadIdx.x; vi < total;
+       vi += (int64_t)kListBlocks * 256) {
+    int pos = -1;
+    if (vi < nl) {
+      pos = (int)(lo + vi);
+    } else {
+      int qg[4];
+      for (int r = 0; r < top_k; ++r) qg[r] = q_groups[(int64_t)b * top_k + r];
+      int64_t rem = vi - nl;
+      for (int r = 0; r < top_k; ++r) {
+        const int64_t cnt = inf[4 + 2 * r];
+        if (rem < cnt) {
+          const int cand = cache_idx[(int64_t)b * Lmax * top_k + inf[3 + 2 * r] + rem];
+          // owned by g_r unless the key also holds a lower query group
+          bool owned = true;
+          const int32_t* kg = cache_groups + ((int64_t)b * Lmax + cand) * top_k;
+          for (int r2 = 0; r2 < top_k; ++r2) {
+            const int g2 = qg[r2];
+            if (g2 >= 0 && g2 < K && g2 < qg[r])
+              for (int r3 = 0; r3 < top_k; ++r3) owned = owned && kg[r3] != g2;
+          }
+          pos = owned ? cand : -1;
+          break;
         }
-        pos = owned ? cand : -1;
-        break;
+        rem -= cnt;
       }
-      rem -= cnt;
     }
+    list[(int64_t)b * per_seq + vi] = pos;
   }
-  list[(int64_t)b * per_seq + vi] = pos;
 }
 
 struct DecodeArgs {
@@ -139,7 +139,9 @@ struct DecodeArgs {
   int64_t per_seq;  // list capacity per sequence
   int B;
   int64_t Lmax;
-  int Hq, Hkv, G, top_k, splits, hpb;  // hpb: query heads per block (<= kDecHeads)
+  int Hq, Hkv, G, top_k, splits;
+  int hpb;  // query heads per unit (<= kDecHeads), all of one kv head
+  int upb;  // units per block: divides the block's lane groups and the units of a sequence
   float sl2;
   float* part_o;   // [B, Hq, splits, DH] unnormalised
   float* part_ml;  // [B, Hq, splits, 2] (running max in log2 units, sum)
@@ -169,16 +171,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// The sequence's resolved key list is cut into `splits` contiguous pieces per (sequence, group
-// of up to 4 query heads of one kv head). Every 16-lane group takes one key at a time: each lane
-// holds 8 dims of the query heads in registers and reads one coalesced 16-byte chunk of the
-// key's K and V rows, the dot products are reduced across the 16 lanes, and a running
-// (max, sum, O) per head absorbs the key. A lane group keeps U keys' rows in flight and loads
-// the positions of its next U keys before absorbing the current ones.
+// The sequence's resolved key list is cut into `splits` contiguous pieces. A head unit is up to 4
+// query heads of one kv head; a block serves `upb` units, so its lane groups split into `upb`
+// units times NG / upb key slots. Groups of one slot take the same key, so when a block's
+// units cover every kv head, each key's K and V rows (all kv heads, contiguous) are read whole
+// by one block. Each lane holds 8 dims of its unit's query heads as bf16 pairs and reads one
+// 16-byte chunk of the key's K and V rows; the dot products are reduced across the 16 lanes
+// with row moves, and a running (max, sum, O) per head absorbs the key. A lane group keeps U
+// keys' rows in flight and loads the positions of its next U keys before absorbing the
+// current ones.
 template <int DH>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
   constexpr int CHK = DH / 8;          // 16-byte chunks per row: lanes per key
-  constexpr int KPW = kWave / CHK;     // keys per wave instruction
+  constexpr int KPW = kWave / CHK;     // lane groups per wave
   constexpr int NG = 4 * KPW;          // lane groups per block
   constexpr int HD = kDecHeads;
   constexpr int U = 4;                 // keys in flight per lane group
@@ -187,11 +192,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int c = l % CHK, grp = wave * KPW + l / CHK;  // chunk of the row, lane group
+  const int upb = a.upb, slots = NG / a.upb;           // units per block, keys taken at once
+  const int ul = grp % upb, slot = grp / upb;
+  const int nub = a.Hq / a.hpb / upb;                  // blocks of units per sequence
   const int64_t lin = blockIdx.x;
   const int sp = (int)(lin % a.splits);
-  const int hgrp = (int)((lin / a.splits) % (a.Hq / a.hpb));  // head group
-  const int b = (int)(lin / ((int64_t)a.splits * (a.Hq / a.hpb)));
-  const int hq0 = hgrp * a.hpb, h = hq0 / a.G;
+  const int ub = (int)((lin / a.splits) % nub);
+  const int b = (int)(lin / ((int64_t)a.splits * nub));
+  const int hq0 = (ub * upb + ul) * a.hpb, h = hq0 / a.G;
   const int nh = a.hpb;
 
   const int32_t* inf = a.info + (int64_t)b * kDecInfo;
@@ -222,14 +230,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const uint16_t* kbase = a.kc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
   const uint16_t* vbase = a.vc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
 
-  // entries v0 + grp + k * NG of the piece, U at a time
+  // entries v0 + slot + k * slots of the piece, U at a time
   int pn[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t j = v0 + grp + (int64_t)u * NG;
+    const int64_t j = v0 + slot + (int64_t)u * slots;
     pn[u] = j < v1 ? lst[j] : -1;
   }
-  for (int64_t j0 = v0 + grp; j0 < v1; j0 += (int64_t)U * NG) {
+  for (int64_t j0 = v0 + slot; j0 < v1; j0 += (int64_t)U * slots) {
     int pk[U];
     i32x4_t kr[U], vr[U];
 #pragma unroll
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {  // positions of the next U keys, behind this batch's rows
-      const int64_t j = j0 + (int64_t)(U + u) * NG;
+      const int64_t j = j0 + (int64_t)(U + u) * slots;
       pn[u] = j < v1 ? lst[j] : -1;
     }
 #pragma unroll
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
     }
   }
 
-  // ---- merge the lane groups' states and write this block's partial per head
+  // ---- merge each unit's key slots and write this block's partial per head
   if (c == 0) {
 #pragma unroll
     for (int hh = 0; hh < HD; ++hh) {
@@ -291,20 +299,21 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 #pragma unroll
     for (int e = 0; e < 8; ++e) red_o[grp][hh][c * 8 + e] = o[hh][e];
   __syncthreads();
-  for (int i = tid; i < nh * DH; i += 256) {
-    const int hh = i / DH, d = i % DH;
+  for (int i = tid; i < upb * nh * DH; i += 256) {
+    const int u = i / (nh * DH), hh = (i / DH) % nh, d = i % DH;
     float M = -INFINITY;
-    for (int g = 0; g < NG; ++g) M = fmaxf(M, red_ml[g][hh][0]);
+    for (int s2 = 0; s2 < slots; ++s2) M = fmaxf(M, red_ml[s2 * upb + u][hh][0]);
     float lsum = 0.f, acc = 0.f;
     if (M != -INFINITY)
-      for (int g = 0; g < NG; ++g) {
+      for (int s2 = 0; s2 < slots; ++s2) {
+        const int g = s2 * upb + u;
         const float m = red_ml[g][hh][0];
         if (m == -INFINITY) continue;
         const float w = fast_exp2(m - M);
         lsum += w * red_ml[g][hh][1];
         acc += w * red_o[g][hh][d];
       }
-    const int64_t pi = ((int64_t)b * a.Hq + hq0 + hh) * a.splits + sp;
+    const int64_t pi = ((int64_t)b * a.Hq + (ub * upb + u) * a.hpb + hh) * a.splits + sp;
     a.part_o[pi * DH + d] = acc;
     if (d == 0) {
       a.part_ml[pi * 2] = M;
@@ -324,17 +333,26 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(const float* __restr
   (void)Hkv;
   (void)G;
   const int d = threadIdx.x;
+  (void)splits;  // always kDecSplits
+  float m[kDecSplits], sm[kDecSplits], po[kDecSplits];
+#pragma unroll
+  for (int s = 0; s < kDecSplits; ++s) {  // every load in flight at once
+    const int64_t pi = bh * kDecSplits + s;
+    const float2 ml = *(const float2*)&part_ml[pi * 2];
+    m[s] = ml.x;
+    sm[s] = ml.y;
+    po[s] = part_o[pi * DH + d];
+  }
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(bh * splits + s) * 2]);
+#pragma unroll
+  for (int s = 0; s < kDecSplits; ++s) M = fmaxf(M, m[s]);
   float den = 0.f, acc = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      int64_t pi = bh * splits + s;
-      float m = part_ml[pi * 2];
-      if (m == -INFINITY) continue;
-      float w = fast_exp2(m - M);
-      den += w * part_ml[pi * 2 + 1];
-      acc += w * part_o[pi * DH + d];
+#pragma unroll
+    for (int s = 0; s < kDecSplits; ++s) {
+      const float w = m[s] == -INFINITY ? 0.f : fast_exp2(m[s] - M);
+      den += w * sm[s];
+      acc += w * po[s];
     }
   }
   float o = den > 0.f ? acc / den : 0.f;
@@ -353,7 +371,8 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
                      q_groups, cache_len, cache_off, cache_idx, s.Lmax, s.K, s.top_k, s.window,
                      info);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * ((per_seq + 255) / 256)), dim3(256),
+  if (s.splits != kDecSplits) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * kListBlocks), dim3(256),
                      0, stream, q_groups, cache_groups, cache_idx, info, s.Lmax, s.K, s.top_k,
                      per_seq, list);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
@@ -375,7 +394,13 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.hpb = s.G < kDecHeads ? s.G : kDecHeads;
-  const int64_t blocks = (int64_t)s.B * (s.Hq / a.hpb) * s.splits;
+  {
+    const int units = s.Hq / a.hpb, ng = s.dh == 128 ? 16 : 32;  // lane groups per block
+    int g = ng;
+    while (units % g != 0) g /= 2;  // ng is a power of two: the largest common power of two
+    a.upb = g;
+  }
+  const int64_t blocks = (int64_t)s.B * (s.Hq / a.hpb / a.upb) * s.splits;
   if (s.dh == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

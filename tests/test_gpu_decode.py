@@ -24,6 +24,8 @@ def run_decode(qd, q_groups, kc, vc, lens, cache_groups, K, window):
     (4, 1000, 16, 2, 128, 16, 3, 1),
     (2, 2000, 32, 8, 128, 64, 2, 256),
     (6, 257, 2, 1, 64, 3, 2, 400),
+    (2, 700, 64, 8, 128, 16, 2, 32),
+    (3, 900, 32, 2, 64, 16, 1, 64),
 ])
 def test_decode_matches_oracle(B, L, Hq, Hkv, dh, K, k, w):
     say(f"decode B={B} L={L} Hq={Hq} Hkv={Hkv} dh={dh} K={K} top_k={k} window={w}")
