@@ -8,7 +8,7 @@ layer; the 1M-token prefill, the batched decode and a dense causal baseline on t
 reported beside it. Kernel times inside focus_attention come from HIP events the library records
 on its own stream around each stage (focus_attention_ex).
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--quick]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--quick] [--decode]
 """
 import argparse
 import ctypes
@@ -385,6 +385,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--decode", action="store_true",
+                    help="only the batched decode workload (prints its own JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB copy, to scale HBM byte counters")
@@ -395,6 +397,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.decode:
+        cfg = {x.name: x for x in CONFIGS}
+        print(json.dumps(decode_bench(cfg["decode_b64_l64k"], 20, 3)), flush=True)
+        return
     hip = Hip()
     if args.calibrate_copy:
         calibration_copy()
