@@ -502,13 +502,38 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, qm[j], sacc[kb], 0, 0, 0);
         }
     }
+    // K fragments are read KPF k-steps ahead of their MFMAs (a rolling window of registers), so
+    // LDS latency overlaps the MFMAs of the steps before
+    constexpr int KPF = 2;
+    bf16x8_t kf[KPF + 1][2];
+#pragma unroll
+    for (int s = 0; s < KPF; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[s][kb] = *(const bf16x8_t*)(lds + krd[s] + par + kb * 32 * RB);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
+      if (s + KPF < NS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t kf = *(const bf16x8_t*)(lds + krd[s] + par + kb * 32 * RB);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb)
+          kf[(s + KPF) % (KPF + 1)][kb] = *(const bf16x8_t*)(lds + krd[s + KPF] + par + kb * 32 * RB);
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KPF + 1)][kb], qreg[s], sacc[kb], 0, 0, 0);
+    }
+    {
+      // keep 2 * KPF operand reads in flight: the scheduler would otherwise sink each read
+      // next to its MFMA (masks: 0x100 LDS read, 0x008 MFMA); the bias step's operands, when
+      // present, are read first like the K fragments
+      constexpr int NM = 2 * (NS + MKS);  // MFMAs of the S product, each with one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
+#pragma unroll
+      for (int i = 0; i < NM - 2 * KPF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KPF, 0);
     }
 
     // ------------------------------------------------------------ mask
