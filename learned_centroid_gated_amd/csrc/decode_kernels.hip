@@ -187,6 +187,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   constexpr int NG = 4 * KPW;          // lane groups per block
   constexpr int HD = kDecHeads;
   constexpr int U = 4;                 // keys in flight per lane group
+  static_assert(U == 4, "the batch maximum below takes four keys");
   __shared__ float red_o[NG][HD][DH];
   __shared__ float red_ml[NG][HD][2];
 
@@ -252,9 +253,49 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
       const int64_t j = j0 + (int64_t)(U + u) * slots;
       pn[u] = j < v1 ? lst[j] : -1;
     }
+    // scores of the batch's U keys for every head (heads past nh are computed and ignored),
+    // all before any reduction so the independent row-move chains interleave
+    float sc[U][HD];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int hh = 0; hh < HD; ++hh) {
+        // bf16 products are exact in fp32; two chains of two pairs each
+        const float d0 = dot2_bf16((uint32_t)qr[hh][1], (uint32_t)kr[u][1],
+                                   dot2_bf16((uint32_t)qr[hh][0], (uint32_t)kr[u][0], 0.f));
+        const float d1 = dot2_bf16((uint32_t)qr[hh][3], (uint32_t)kr[u][3],
+                                   dot2_bf16((uint32_t)qr[hh][2], (uint32_t)kr[u][2], 0.f));
+        sc[u][hh] = d0 + d1;
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int hh = 0; hh < HD; ++hh) {
+        const float x = group_sum<CHK>(sc[u][hh]) * a.sl2;
+        sc[u][hh] = pk[u] >= 0 ? x : -INFINITY;  // pk is uniform within the lane group
+      }
+    // lazy running max, one test per batch: rescale only when a score passes the reference by
+    // 2^8, so every weight below stays under 2^8
+    float bmax[HD];
+    bool bump = false;
+#pragma unroll
+    for (int hh = 0; hh < HD; ++hh) {
+      bmax[hh] = fmaxf(fmaxf(sc[0][hh], sc[1][hh]), fmaxf(sc[2][hh], sc[3][hh]));
+      bump = bump || bmax[hh] > m_run[hh] + 8.f;
+    }
+    if (bump) {
+#pragma unroll
+      for (int hh = 0; hh < HD; ++hh) {
+        const bool bh = bmax[hh] > m_run[hh] + 8.f;
+        const float alpha = !bh ? 1.f : m_run[hh] == -INFINITY ? 0.f : fast_exp2(m_run[hh] - bmax[hh]);
+        l_run[hh] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
+        m_run[hh] = bh ? bmax[hh] : m_run[hh];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (pk[u] < 0) continue;  // uniform within the lane group
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -263,22 +304,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
       }
 #pragma unroll
       for (int hh = 0; hh < HD; ++hh) {
-        if (hh >= nh) break;
-        // bf16 products are exact in fp32; two chains of two pairs each
-        const float d0 = dot2_bf16((uint32_t)qr[hh][1], (uint32_t)kr[u][1],
-                                   dot2_bf16((uint32_t)qr[hh][0], (uint32_t)kr[u][0], 0.f));
-        const float d1 = dot2_bf16((uint32_t)qr[hh][3], (uint32_t)kr[u][3],
-                                   dot2_bf16((uint32_t)qr[hh][2], (uint32_t)kr[u][2], 0.f));
-        const float sdot = group_sum<CHK>(d0 + d1) * a.sl2;
-        // lazy running max: rescale only when the score passes the reference by 2^8
-        if (sdot > m_run[hh] + 8.f) {
-          const float alpha = m_run[hh] == -INFINITY ? 0.f : fast_exp2(m_run[hh] - sdot);
-          l_run[hh] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
-          m_run[hh] = sdot;
-        }
-        const float pw = fast_exp2(sdot - m_run[hh]);
+        const float m_use = m_run[hh] == -INFINITY ? 0.f : m_run[hh];
+        const float pw = fast_exp2(sc[u][hh] - m_use);  // 0 for a dropped entry
         l_run[hh] += pw;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pw, vf[e], o[hh][e]);
