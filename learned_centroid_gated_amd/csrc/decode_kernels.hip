@@ -196,7 +196,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const int upb = a.upb, slots = NG / a.upb;           // units per block, keys taken at once
   const int ul = grp % upb, slot = grp / upb;
   const int nub = a.Hq / a.hpb / upb;                  // blocks of units per sequence
-  const int64_t lin = blockIdx.x;
+  // each XCD takes a contiguous range of sequences, so its address-translation working set is
+  // its own sequences' caches rather than every cache
+  const int64_t lin = xcd_remap(blockIdx.x, (int64_t)a.B * nub * a.splits);
+  if (lin < 0) return;  // whole block: before any barrier
   const int sp = (int)(lin % a.splits);
   const int ub = (int)((lin / a.splits) % nub);
   const int b = (int)(lin / ((int64_t)a.splits * nub));
@@ -427,7 +430,7 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
     while (units % g != 0) g /= 2;  // ng is a power of two: the largest common power of two
     a.upb = g;
   }
-  const int64_t blocks = (int64_t)s.B * (s.Hq / a.hpb / a.upb) * s.splits;
+  const int64_t blocks = xcd_grid((int64_t)s.B * (s.Hq / a.hpb / a.upb) * s.splits);
   if (s.dh == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
