@@ -364,16 +364,27 @@ hipError_t launch_fill_f32(float* p, float value, int64_t count, hipStream_t str
 // ============================================================================ row layouts
 // A row of K scores is spread over LPR lanes; lane q of the row holds columns
 // 4q + 4*LPR*c + e (c < CPL, e < 4). Rows per wave: 64 / LPR.
+// Row reductions over the row's LPR lanes (an aligned group): within a 16-lane row by VALU
+// lane moves (pairs, quads, half-row mirror, row mirror: each step combines two disjoint
+// halves of the group so far), across rows by lane shuffles.
 template <int LPR>
 __device__ __forceinline__ float row_max(float x) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) x = fmaxf(x, shfl_xor_f(x, o));
+  if constexpr (LPR >= 2) x = fmaxf(x, dpp_move<0xB1>(x));
+  if constexpr (LPR >= 4) x = fmaxf(x, dpp_move<0x4E>(x));
+  if constexpr (LPR >= 8) x = fmaxf(x, dpp_move<0x141>(x));
+  if constexpr (LPR >= 16) x = fmaxf(x, dpp_move<0x140>(x));
+  if constexpr (LPR >= 32) x = fmaxf(x, shfl_xor_f(x, 16));
+  if constexpr (LPR >= 64) x = fmaxf(x, shfl_xor_f(x, 32));
   return x;
 }
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) x += shfl_xor_f(x, o);
+  if constexpr (LPR >= 2) x += dpp_move<0xB1>(x);
+  if constexpr (LPR >= 4) x += dpp_move<0x4E>(x);
+  if constexpr (LPR >= 8) x += dpp_move<0x141>(x);
+  if constexpr (LPR >= 16) x += dpp_move<0x140>(x);
+  if constexpr (LPR >= 32) x += shfl_xor_f(x, 16);
+  if constexpr (LPR >= 64) x += shfl_xor_f(x, 32);
   return x;
 }
 
@@ -415,8 +426,8 @@ __global__ __launch_bounds__(256) void sinkhorn_rows_kernel(const float* __restr
       cs[4 * c + e] = 0.f;
     }
 
-  // the next row's scores are loaded while this row is reduced
-  auto load_row = [&](int64_t row, f32x4_t (&x)[CPL]) {
+  // rows are loaded two row groups ahead of their reduction, into two buffers used in turn
+  auto load_row = [&](int64_t row, f32x4_t (&x)[CPL]) __attribute__((always_inline)) {
     const float* sp = S + row * ldS;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -424,15 +435,17 @@ __global__ __launch_bounds__(256) void sinkhorn_rows_kernel(const float* __restr
       x[c] = (row < r_end && col < K) ? *(const f32x4_t*)(sp + col) : f32x4_t{};
     }
   };
-  f32x4_t nxt[CPL];
-  load_row(r_begin + wave * RPW + rg, nxt);
-  for (int64_t row = r_begin + wave * RPW + rg; row < r_end; row += 4 * RPW) {
+  f32x4_t nxt[2][CPL];
+  const int64_t row0 = r_begin + wave * RPW + rg;
+  load_row(row0, nxt[0]);
+  load_row(row0 + 4 * RPW, nxt[1]);
+  auto one_row = [&](int64_t row, f32x4_t (&buf)[CPL]) __attribute__((always_inline)) {
     float s[NC];
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * c + e] = nxt[c][e];
-    load_row(row + 4 * RPW, nxt);
+      for (int e = 0; e < 4; ++e) s[4 * c + e] = buf[c][e];
+    load_row(row + 8 * RPW, buf);
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NC; ++i)
@@ -457,14 +470,32 @@ __global__ __launch_bounds__(256) void sinkhorn_rows_kernel(const float* __restr
         cs[i] += e;
       }
     }
+  };
+  for (int64_t row = row0; row < r_end; row += 8 * RPW) {
+    one_row(row, nxt[0]);
+    if (row + 4 * RPW < r_end) one_row(row + 4 * RPW, nxt[1]);
   }
-  // combine the row groups of the wave (lanes with equal q)
+  // combine the row groups of the wave (lanes with equal q, i.e. lane l with l ^ o for o >= LPR):
+  // l ^ 8 by a row rotation, l ^ 16 and l ^ 32 by the row-swapping permutes (each lane then holds
+  // its own and its partner's value, in some order), smaller distances by lane shuffles
 #pragma unroll
   for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      float m2 = shfl_xor_f(cm[i], o), s2 = shfl_xor_f(cs[i], o);
-      ms_merge(cm[i], cs[i], m2, s2);
+      if (o == 16 || o == 32) {
+        const auto pm = o == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(cm[i]), __float_as_uint(cm[i]), false, false)
+                                : __builtin_amdgcn_permlane32_swap(__float_as_uint(cm[i]), __float_as_uint(cm[i]), false, false);
+        const auto ps = o == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(cs[i]), __float_as_uint(cs[i]), false, false)
+                                : __builtin_amdgcn_permlane32_swap(__float_as_uint(cs[i]), __float_as_uint(cs[i]), false, false);
+        float m = __uint_as_float(pm[0]), sm = __uint_as_float(ps[0]);
+        ms_merge(m, sm, __uint_as_float(pm[1]), __uint_as_float(ps[1]));
+        cm[i] = m;
+        cs[i] = sm;
+      } else {
+        const float m2 = o == 8 ? dpp_move<0x128>(cm[i]) : shfl_xor_f(cm[i], o);  // row_ror:8
+        const float s2 = o == 8 ? dpp_move<0x128>(cs[i]) : shfl_xor_f(cs[i], o);
+        ms_merge(cm[i], cs[i], m2, s2);
+      }
     }
   if (rg == 0) {
 #pragma unroll

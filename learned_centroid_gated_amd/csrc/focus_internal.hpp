@@ -40,6 +40,16 @@ __device__ __forceinline__ float pair32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// x of another lane of the same 16-lane row, moved on the VALU (data-parallel-primitive
+// control CTRL: 0xB1 / 0x4E swap lanes l^1 / l^2 within quads, 0x141 mirrors the 8-lane half
+// row, 0x140 the 16-lane row, 0x128 rotates the row by 8, i.e. l^8). Every lane is a valid
+// source for these controls.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
