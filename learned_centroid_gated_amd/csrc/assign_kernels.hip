@@ -649,15 +649,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S,
           bv = b[i];
           bi = colx[i];
         }
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) {
-        float v2 = shfl_xor_f(bv, o);
-        int i2 = shfl_xor_i(bi, o);
+      // argmax over the row's lanes: `better` is a strict total order, so any pairing that
+      // combines disjoint halves of the group gives every lane the same winner; within a 16-lane
+      // row the pairs move on the VALU
+      auto take = [&](float v2, int i2) __attribute__((always_inline)) {
         if (better(v2, i2, bv, bi)) {
           bv = v2;
           bi = i2;
         }
-      }
+      };
+      if constexpr (LPR >= 2) take(dpp_move<0xB1>(bv), dpp_move_i<0xB1>(bi));
+      if constexpr (LPR >= 4) take(dpp_move<0x4E>(bv), dpp_move_i<0x4E>(bi));
+      if constexpr (LPR >= 8) take(dpp_move<0x141>(bv), dpp_move_i<0x141>(bi));
+      if constexpr (LPR >= 16) take(dpp_move<0x140>(bv), dpp_move_i<0x140>(bi));
+      if constexpr (LPR >= 32) take(shfl_xor_f(bv, 16), shfl_xor_i(bi, 16));
+      if constexpr (LPR >= 64) take(shfl_xor_f(bv, 32), shfl_xor_i(bi, 32));
       sel[r] = bi;
 #pragma unroll
       for (int i = 0; i < NC; ++i)

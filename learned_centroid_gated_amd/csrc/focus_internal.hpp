@@ -50,6 +50,11 @@ __device__ __forceinline__ float dpp_move(float x) {
                                                                0xF, 0xF, false));
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_move_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
