@@ -3,10 +3,11 @@
 
 A step is one pass of the prefill hot path over one synthetic sequence with every input already
 resident in HBM: focus_assign (scores, Sinkhorn, top-k) -> focus_bucket -> focus_attention
-(gather, group pass, window pass with the merge in its epilogue). The headline line is the 128K-token 70B-shaped GQA
-layer; the 1M-token prefill, the batched decode and a dense causal baseline on the same GPU are
-reported beside it. Kernel times inside focus_attention come from HIP events the library records
-on its own stream around each stage (focus_attention_ex).
+(gather, group pass, window pass with the merge in its epilogue). The headline line is the
+128K-token 70B-shaped GQA layer; the 1M-token prefill, the batched decode, a dense causal
+baseline on the same GPU and the training-time soft-gate forward are reported beside it. Kernel
+times inside focus_attention come from HIP events the library records on its own stream around
+each stage (focus_attention_ex).
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--quick] [--decode]
 """
@@ -26,7 +27,8 @@ sys.path.insert(0, ROOT)
 
 from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_size,  # noqa: E402
                                         focus_attention, focus_attention_workspace_size,
-                                        focus_bucket, focus_bucket_workspace_size, focus_decode)
+                                        focus_bucket, focus_bucket_workspace_size, focus_decode,
+                                        focus_soft_attention)
 from learned_centroid_gated_amd import _lib  # noqa: E402
 from synth import CONFIGS, assign_inputs, qkv_inputs, random_groups  # noqa: E402
 
@@ -269,6 +271,19 @@ def dense_baseline(c, st, hip, reps=2):
     causal_flops = 4.0 * c.dh * c.Hq * c.n * (c.n + 1) / 2
     res = {"own_window_kernel_ms": own_ms,
            "own_window_kernel_tflops": causal_flops / (own_ms * 1e-3) / 1e12}
+    # the training-time soft gate's forward over the same inputs: every causal pair, far pairs
+    # biased by log sigmoid(lambda * (share - 1/2)) from the same memberships (lambda = 10)
+    times = []
+    for r in range(reps + 1):
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        focus_soft_attention(q, k, v, st["groups"], c.K, c.window, 10.0, out=out, lse=lse)
+        e0.record()
+        torch.cuda.synchronize()
+        if r:
+            times.append(s0.elapsed_time(e0))
+    res["soft_gate_forward_ms"] = float(np.mean(times))
+    res["soft_gate_forward_tflops"] = causal_flops / (res["soft_gate_forward_ms"] * 1e-3) / 1e12
     try:
         G = c.Hq // c.Hkv
         qt = q.permute(1, 0, 2).unsqueeze(0)

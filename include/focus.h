@@ -157,6 +157,32 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        void* const* stage_events, int num_events);
 
 /* ------------------------------------------------------------------------------------
+ * focus_soft_attention - the training-time soft gate (ZH 2.1.2 gate formula), forward only:
+ * exact softmax over every causal pair, with far pairs' weights multiplied by the gate
+ * sigmoid(lambda * a_ij):
+ *
+ *   a_ij       = [groups[i] and groups[j] share a group] - 1/2
+ *   logit_ij   = scale * q[i,h] . k[j,h/G] + (i - j < window ? 0 : log sigmoid(lambda * a_ij))
+ *   out[i, h]  = sum over j <= i of softmax_j(logit_ij) * v[j,h/G]
+ *   lse[i, h]  = natural log of sum over j <= i of exp(logit_ij)
+ *
+ * (the printed form multiplies the logit itself by the gate, which does not approach the hard
+ * mask as lambda grows; this reading does, and reduces to focus_attention's pair rule in the
+ * limit). Dense causal cost: every pair j <= i is computed.
+ *
+ *   q, k, v, n, Hq, Hkv, d_head, scale, out, lse   as for focus_attention.
+ *   groups   device, [n, top_k] int32; ids outside [0, K) never match.
+ *   K        1 <= K <= 1024; top_k 1 <= top_k <= min(K, 4).
+ *   window   >= 0.
+ *   lambda   finite gate sharpness.
+ * Needs no workspace. Asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------ */
+int focus_soft_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         int64_t n, int Hq, int Hkv, int d_head,
+                         const int32_t* groups, int K, int top_k, int64_t window, float lambda,
+                         float scale, uint16_t* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * focus_decode - one new token per sequence against its own cache (ZH 2.1.3 inference).
  *
  * Sequence b holds L_b = cache_len[b] tokens; its new token is the last one, at position

@@ -12,5 +12,6 @@ from .focus import (  # noqa: F401
     focus_bucket_workspace_size,
     focus_decode,
     focus_decode_workspace_size,
+    focus_soft_attention,
 )
 from ._lib import LIB_PATH, FocusError, lib, status_string  # noqa: F401

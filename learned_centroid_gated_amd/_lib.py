@@ -23,6 +23,8 @@ SIGNATURES = {
     "focus_attention_ex": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_p, c_p, c_p,
                                    c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p,
                                    ctypes.POINTER(c_p), c_int]),
+    "focus_soft_attention": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_int, c_int,
+                                     c_i64, c_f, c_f, c_p, c_p, c_p]),
     "focus_decode_workspace_size": (c_sz, [c_int, c_i64, c_int, c_int, c_int, c_int, c_int]),
     "focus_decode": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int, c_int,
                              c_int, c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p]),

@@ -192,6 +192,9 @@ struct FlashArgs {
   int w_max;                // group: work items per kv head (upper bound)
   int K;
   int tiles_per_head;       // window: ceil(n / T)
+  const int32_t* groups;    // soft gate: [n, top_k] memberships
+  float soft_b0, soft_b1;   // soft gate: far-pair logit bias without / with a shared group,
+                            // in raw q.k units (log sigmoid(lambda * (share - 1/2)) / scale)
 };
 
 constexpr int KT = 64;  // keys per kv tile
@@ -230,7 +233,11 @@ constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully 
 // NLOW = top_k - 1: lower groups per membership that matter for the ownership rule (group
 // pass), and top_k - 1 for the window pass, whose merge reads top_k group parts per token.
 // MKS = 16-token k-steps of the MFMA ownership bias (0: per-element compare instead).
-template <int DH, bool GROUP, int NLOW, int MKS>
+// SOFT (window pass only): the training-time soft gate instead of the hard pair rule: every
+// causal pair is attended, far pairs with a logit bias that depends on whether the two tokens
+// share a group (the tile's key groups are staged in LDS like the group pass's key records),
+// and there are no group parts to merge.
+template <int DH, bool GROUP, int NLOW, int MKS, bool SOFT = false>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   using Smem = FlashSmem<DH, MKS>;
   constexpr int CH = DH / 8;             // 16-byte chunks per key row
@@ -241,6 +248,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   constexpr int RB = 2 * DH;             // bytes per key row
   static_assert(MKS == 0 || (GROUP && NLOW > 0), "ownership bias only in the group pass");
   static_assert(NLOW >= 0 && NLOW <= 3, "top_k is 1 to 4");
+  static_assert(!(SOFT && GROUP), "the soft gate runs on the window pass");
   __shared__ __attribute__((aligned(1024))) Smem smem[2];  // double buffer: one barrier per tile
   __shared__ __attribute__((aligned(16))) int qlow_s[3][32];  // MKS > 0: query tokens' lower groups, -2 if none
 
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   } else {
     q0 = item * a.T;
     q1 = (int)min((int64_t)q0 + a.T, a.n);
-    kv_lo = max(q0 - window + 1, 0);
+    kv_lo = SOFT ? 0 : max(q0 - window + 1, 0);
   }
   const int kv_hi = q1 - 1;  // last key index any query of the tile may see
 
@@ -306,7 +314,16 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   float Lr[GROUP ? 1 : TK];
   if constexpr (!GROUP) {
 #pragma unroll
-    for (int r = 0; r < TK; ++r) srow[r] = qvalid ? a.slot[(int64_t)qi * TK + r] : -1;
+    for (int r = 0; r < TK; ++r) srow[r] = (qvalid && !SOFT) ? a.slot[(int64_t)qi * TK + r] : -1;
+  }
+  // soft gate: this row's token's groups (-2 where none or out of range: never matches a key)
+  int qg[SOFT ? TK : 1];
+  if constexpr (SOFT) {
+#pragma unroll
+    for (int c = 0; c < TK; ++c) {
+      const int g = qvalid ? a.groups[(int64_t)qi * TK + c] : -2;
+      qg[c] = (g >= 0 && g < a.K) ? g : -2;
+    }
   }
 
   bf16x8_t qreg[NS];
@@ -334,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
 
   // ---------------------------------------------------------------- kv tile range
-  if constexpr (!GROUP) ntiles = window > 0 ? (kv_hi - kv_lo) / KT + 1 : 0;
+  if constexpr (!GROUP) ntiles = (SOFT || window > 0) ? (kv_hi - kv_lo) / KT + 1 : 0;
 
   f32x16_t oacc[ND];
 #pragma unroll
@@ -426,6 +443,16 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
         }
       }
     }
+    if constexpr (SOFT) {
+      // the key's groups (-1 where none, out of range or past the last key)
+      if (kkey < KT) {
+#pragma unroll
+        for (int c = 0; c < TK; ++c) {
+          const int g = kkey <= nrow ? a.groups[(int64_t)(ks + kkey) * TK + c] : -1;
+          ireg[c] = (g >= 0 && g < a.K) ? g : -1;
+        }
+      }
+    }
   };
   // Waits for this wave's loads go through the builtin (not inline asm), so the compiler's own
   // wait tracking sees them. They are placed on every path into the tile loop and at the end of
@@ -462,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       } else {
         *(i32x4_t*)dst = i32x4_t{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
       }
-    } else if constexpr (GROUP) {
+    } else if constexpr (GROUP || SOFT) {  // soft gate: kpos / klow hold the key's groups
       if (tid < KT) {
         sb.kpos[tid] = ireg[0];
 #pragma unroll
@@ -485,9 +512,9 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
         cls = (NLOW == 0 || MKS > 0) ? kFull : kFar;
       else cls = kEdge;
     } else {
-      if (ks > wq_hi || wq_lo - k_last >= window) cls = kSkip;
+      if (ks > wq_hi || (!SOFT && wq_lo - k_last >= window)) cls = kSkip;
       else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
-      else cls = kEdge;
+      else cls = kEdge;  // soft gate: also every tile with far pairs
     }
     if (cls == kSkip) return;
 
@@ -561,6 +588,24 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 #pragma unroll
                   for (int c1 = 0; c1 < NLOW; ++c1) ok[e] = ok[e] && kl[e] != qlow[c1];
               }
+            }
+          } else if constexpr (SOFT) {
+            // causal; far pairs get the gate's bias, by whether the tokens share a group
+            bool share[4] = {false, false, false, false};
+#pragma unroll
+            for (int c2 = 0; c2 < TK; ++c2) {
+              const i32x4_t kg = c2 == 0 ? *(const i32x4_t*)&sm.kpos[kk0]
+                                         : *(const i32x4_t*)&sm.klow[c2 > 0 ? c2 - 1 : 0][kk0];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c1 = 0; c1 < TK; ++c1) share[e] = share[e] || kg[e] == qg[c1];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int dd = qi - (ks + kk0 + e);
+              ok[e] = dd >= 0;
+              if (dd >= window) sacc[kb][4 * q4 + e] += share[e] ? a.soft_b1 : a.soft_b0;
             }
           } else {
 #pragma unroll
@@ -636,7 +681,8 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   if constexpr (!GROUP) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-    for (int r = 0; r < TK; ++r) Lr[r] = srow[r] >= 0 ? a.lseg[(int64_t)srow[r] * a.Hq + hq] : -INFINITY;
+    for (int r = 0; r < TK; ++r)
+      Lr[r] = (!SOFT && srow[r] >= 0) ? a.lseg[(int64_t)srow[r] * a.Hq + hq] : -INFINITY;
   }
   if (ntiles > 0) issue_tile(kv_lo, smem[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -751,7 +797,8 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
         for (int r = 0; r < TK; ++r) {
           gc[ib][r] = __shfl(cr[r], row, kWave);  // every lane takes part in the shuffles
           const int sl = max(__shfl(srow[r], row, kWave), 0);
-          gx[ib][r] = *(const f16x8_t*)(a.og + ((int64_t)sl * a.Hq + hr) * DH + 8 * cl);
+          if constexpr (SOFT) gx[ib][r] = f16x8_t{};  // no group parts (their weight is 0)
+          else gx[ib][r] = *(const f16x8_t*)(a.og + ((int64_t)sl * a.Hq + hr) * DH + 8 * cl);
         }
       }
       if (i0 == 0) {
@@ -799,12 +846,14 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
 }
 
-template <bool GROUP, int NLOW, int MKS>
+template <bool GROUP, int NLOW, int MKS, bool SOFT = false>
 static void flash_dispatch_dh(const FlashArgs& fa, int dh, int64_t blocks, hipStream_t stream) {
   if (dh == 128)
-    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS>), dim3(blocks), dim3(256), 0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS, SOFT>), dim3(blocks), dim3(256), 0,
+                       stream, fa);
   else
-    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS>), dim3(blocks), dim3(256), 0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS, SOFT>), dim3(blocks), dim3(256), 0,
+                       stream, fa);
 }
 
 template <int NLOW>
@@ -883,6 +932,40 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
     case 2: flash_dispatch_dh<false, 1, 0>(fa, s.dh, blocks, stream); break;
     case 3: flash_dispatch_dh<false, 2, 0>(fa, s.dh, blocks, stream); break;
     default: flash_dispatch_dh<false, 3, 0>(fa, s.dh, blocks, stream); break;
+  }
+  return hipGetLastError();
+}
+
+// The soft gate's forward: the window kernel over every causal pair (see flash_kernel's SOFT).
+hipError_t launch_soft_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* groups, const AttnShape& s, float bias_none,
+                                 float bias_share, uint16_t* out, float* lse, hipStream_t stream) {
+  FlashArgs fa{};
+  fa.q = q;
+  fa.k = k;
+  fa.v = v;
+  fa.out = out;
+  fa.lse = lse;
+  fa.groups = groups;
+  fa.top_k = s.top_k;
+  fa.K = s.K;
+  fa.n = s.n;
+  fa.Hq = s.Hq;
+  fa.Hkv = s.Hkv;
+  fa.G = s.G;
+  fa.T = attn_tile_tokens(s.G);
+  fa.window = (int)(s.window < s.n ? s.window : s.n);
+  fa.sl2 = s.scale * kLog2e;
+  fa.soft_b0 = bias_none / s.scale;
+  fa.soft_b1 = bias_share / s.scale;
+  fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
+  const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
+  if (blocks <= 0) return hipSuccess;
+  switch (s.top_k) {
+    case 1: flash_dispatch_dh<false, 0, 0, true>(fa, s.dh, blocks, stream); break;
+    case 2: flash_dispatch_dh<false, 1, 0, true>(fa, s.dh, blocks, stream); break;
+    case 3: flash_dispatch_dh<false, 2, 0, true>(fa, s.dh, blocks, stream); break;
+    default: flash_dispatch_dh<false, 3, 0, true>(fa, s.dh, blocks, stream); break;
   }
   return hipGetLastError();
 }

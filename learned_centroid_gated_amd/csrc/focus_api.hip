@@ -289,6 +289,40 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   return hip_status(e);
 }
 
+int focus_soft_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
+                         int Hq, int Hkv, int d_head, const int32_t* groups, int K, int top_k,
+                         int64_t window, float lambda, float scale, uint16_t* out, float* lse,
+                         void* stream) {
+  if (n < 0 || window < 0 || isnan(lambda) || isinf(lambda)) return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  if (n * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (n == 0) return FOCUS_OK;
+  if (!q || !k || !v || !groups || !out || !lse) return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(groups) || !aligned16(out) ||
+      !aligned4(lse))
+    return FOCUS_ERR_ALIGN;
+  AttnShape s{};
+  s.n = n;
+  s.nk = n * top_k;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
+  s.K = K;
+  s.top_k = top_k;
+  s.window = window < n + 1 ? window : n + 1;
+  s.scale = sc;
+  // far-pair bias log sigmoid(lambda * a), a = +1/2 (shared group) or -1/2, as -log1p(exp(-x))
+  auto log_sigmoid = [](double x) { return x >= 0 ? -log1p(exp(-x)) : x - log1p(exp(x)); };
+  const float b_share = (float)log_sigmoid(0.5 * (double)lambda);
+  const float b_none = (float)log_sigmoid(-0.5 * (double)lambda);
+  return hip_status(launch_soft_attention(q, k, v, groups, s, b_none, b_share, out, lse,
+                                          (hipStream_t)stream));
+}
+
 int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int Hq,
                     int Hkv, int d_head, const int32_t* groups, const int32_t* offsets,
                     const int32_t* idx, const int32_t* slot, int K, int top_k, int64_t window,

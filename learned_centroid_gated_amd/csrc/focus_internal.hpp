@@ -152,6 +152,11 @@ hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const u
                                    const _Float16* og, const float* lseg, const int32_t* slot,
                                    const AttnShape& s, uint16_t* out, float* lse,
                                    hipStream_t stream);
+// Soft-gate forward over every causal pair: far-pair logits get bias_none / bias_share
+// (natural-log units) by whether the tokens share a group.
+hipError_t launch_soft_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* groups, const AttnShape& s, float bias_none,
+                                 float bias_share, uint16_t* out, float* lse, hipStream_t stream);
 int attn_tile_tokens(int G);  // query tokens per attention tile: 128 / G
 
 // Decode.

@@ -122,6 +122,27 @@ def focus_attention(q, k, v, groups, offsets, idx, slot, K, window, scale=0.0, o
     return out, lse
 
 
+# ------------------------------------------------------------------ focus_soft_attention
+def focus_soft_attention(q, k, v, groups, K, window, lam, scale=0.0, out=None, lse=None,
+                         stream=None):
+    """Training-time soft-gated attention over all causal pairs, forward: returns
+    (out [n, Hq, dh] bf16, lse [n, Hq] fp32)."""
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, dev)
+    _need(groups, "groups", torch.int32, dev)
+    n, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    top_k = groups.shape[-1]
+    if out is None:
+        out = torch.empty((n, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((n, Hq), dtype=torch.float32, device=dev)
+    _lib_call("focus_soft_attention", _ptr(q), _ptr(k), _ptr(v), n, Hq, Hkv, dh, _ptr(groups), K,
+              top_k, int(window), float(lam), float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    return out, lse
+
+
 # ------------------------------------------------------------------ focus_decode
 def focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k):
     return _lib.lib().focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k)

@@ -261,13 +261,16 @@ def _soft_gate_logits(q, k, groups, window, lam, scale, literal):
     return np.where((j <= i)[None], s, -np.inf)
 
 
-def soft_gate_ref(q, k, v, groups, window, lam, scale=None, literal=False):
+def soft_gate_ref(q, k, v, groups, window, lam, scale=None, literal=False, with_lse=False):
     """Training-time soft gate over all causal pairs (ZH 2.1.2 formula), weight reading by
     default; literal=True applies the printed form (gate multiplies the logit).
-    Returns out [n, Hq, dh].
+    Returns out [n, Hq, dh], and lse [n, Hq] (natural log of the sum of exp of the gated
+    logits) as well when with_lse.
     """
     s = _soft_gate_logits(q, k, groups, window, lam, scale, literal)
     G = q.shape[1] // k.shape[1]
     vv = _widen(v)[:, np.arange(q.shape[1]) // G, :]
-    p = np.exp(s - _logsumexp(s, axis=2)[:, :, None])
-    return np.einsum("hij,jhd->ihd", p, vv)
+    lse = _logsumexp(s, axis=2)                                 # [Hq, n]
+    p = np.exp(s - lse[:, :, None])
+    out = np.einsum("hij,jhd->ihd", p, vv)
+    return (out, lse.T.copy()) if with_lse else out

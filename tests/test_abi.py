@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -133,6 +133,32 @@ def test_attention_workspace_size(lib):
     # gathered K/V (bf16), fp16 group partials, their log-sum-exp and the key records
     floor = n * k * 2 * Hkv * dh * 2 + n * k * Hq * dh * 2 + n * k * Hq * 4 + n * k * 16
     assert f(n, Hq, Hkv, dh, K, k) >= floor
+
+
+def _soft(lib, q=P, k=P, v=P, n=256, Hq=8, Hkv=2, dh=128, g=P, K=16, top_k=2, window=32,
+          lam=10.0, scale=0.0, out=P, lse=P):
+    return lib.focus_soft_attention(q, k, v, n, Hq, Hkv, dh, g, K, top_k, window, lam, scale, out,
+                                    lse, None)
+
+
+def test_soft_attention_validation(lib):
+    assert _soft(lib, n=-1) == ARG
+    assert _soft(lib, window=-1) == ARG
+    assert _soft(lib, lam=math.nan) == ARG
+    assert _soft(lib, lam=math.inf) == ARG
+    assert _soft(lib, scale=math.nan) == ARG
+    assert _soft(lib, Hq=6, Hkv=4) == ARG
+    assert _soft(lib, Hq=6, Hkv=2) == UNSUP
+    assert _soft(lib, dh=96) == UNSUP
+    assert _soft(lib, K=0) == ARG
+    assert _soft(lib, top_k=5, K=16) == UNSUP
+    assert _soft(lib, n=1 << 30, top_k=2) == SHAPE
+    assert _soft(lib, q=None) == ARG
+    assert _soft(lib, g=None) == ARG
+    assert _soft(lib, lse=None) == ARG
+    assert _soft(lib, k=MIS) == ALIGN
+    assert _soft(lib, out=MIS) == ALIGN
+    assert _soft(lib, n=0, q=None) == OK  # empty: nothing enqueued
 
 
 def _decode(lib, q=P, qg=P, kc=P, vc=P, ln=P, cg=P, co=P, ci=P, B=4, L=1024, Hq=8, Hkv=2, dh=128,

@@ -1,0 +1,56 @@
+"""focus_soft_attention (the training-time soft gate, forward) on the GPU against the oracle.
+
+Every causal pair is attended; far pairs carry log sigmoid(lambda * (share - 1/2)). Element-wise
+on every row, over sweeps of n (ragged tails), window (none, some, all local), top-k, GQA ratio,
+head size and lambda; plus the large-lambda limit, which must reach focus_attention's hard
+pair rule."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bf16_dev, check_attention, i32_dev, say, to_np
+from oracle import soft_gate_ref
+from synth import qkv_inputs, random_groups
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # n, Hq, Hkv, dh, K, top_k, window, lambda
+    (1, 1, 1, 64, 1, 1, 0, 3.0),
+    (65, 2, 1, 128, 4, 1, 8, 4.0),
+    (257, 4, 2, 128, 8, 1, 16, 4.0),
+    (600, 8, 2, 64, 5, 2, 32, 10.0),
+    (1000, 16, 4, 128, 16, 2, 0, 1.0),
+    (513, 2, 1, 128, 3, 3, 700, 2.0),
+    (300, 8, 8, 64, 4, 4, 64, 50.0),
+    (777, 8, 1, 128, 12, 2, 100, -3.0),
+]
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,dh,K,k,w,lam", CASES)
+def test_soft_matches_oracle(n, Hq, Hkv, dh, K, k, w, lam):
+    from learned_centroid_gated_amd import focus_soft_attention
+    say(f"soft n={n} Hq={Hq} Hkv={Hkv} dh={dh} K={K} top_k={k} window={w} lambda={lam}")
+    t = qkv_inputs(n, Hq, Hkv, dh, index=0, salt=500 + n)
+    groups = random_groups(n, K, k, np.random.default_rng(n + K))
+    out, lse = focus_soft_attention(bf16_dev(t["q"]), bf16_dev(t["k"]), bf16_dev(t["v"]),
+                                    i32_dev(groups), K, w, lam)
+    torch.cuda.synchronize()
+    o_ref, l_ref = soft_gate_ref(t["q"], t["k"], t["v"], groups, w, lam, with_lse=True)
+    check_attention(out, lse, o_ref, l_ref, "soft")
+
+
+def test_soft_large_lambda_reaches_hard_rule():
+    from learned_centroid_gated_amd import focus_attention, focus_bucket, focus_soft_attention
+    n, Hq, Hkv, dh, K, k, w = 1500, 8, 2, 128, 16, 2, 64
+    t = qkv_inputs(n, Hq, Hkv, dh, index=0, salt=77)
+    groups = random_groups(n, K, k, np.random.default_rng(5))
+    q, kk, v, g = bf16_dev(t["q"]), bf16_dev(t["k"]), bf16_dev(t["v"]), i32_dev(groups)
+    out_s, lse_s = focus_soft_attention(q, kk, v, g, K, w, 200.0)
+    off, idx, slot = focus_bucket(g, K)
+    out_h, lse_h = focus_attention(q, kk, v, g, off, idx, slot, K, w)
+    torch.cuda.synchronize()
+    d = np.abs(to_np(out_s) - to_np(out_h))
+    dl = np.abs(to_np(lse_s) - to_np(lse_h))
+    say(f"  soft(lambda=200) vs hard: max|dO|={d.max():.2e} max|dLSE|={dl.max():.2e}")
+    assert d.max() <= 2e-2 and dl.max() <= 2e-3

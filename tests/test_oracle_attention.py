@@ -210,3 +210,19 @@ def test_soft_gate_approaches_hard_mask():
     # the printed form (gate multiplies the logit) keeps e^0 weight on gated pairs
     lit = np.abs(soft_gate_ref(t["q"], t["k"], t["v"], groups, w, 100.0, literal=True) - hard).max()
     assert lit > 0.05
+
+
+def test_soft_gate_lse_all_local_is_causal_attention():
+    # window >= n: every pair is local, no gate applies, and the soft forward is plain causal
+    # attention; its lse must then equal the hard rule's (which also allows every causal pair)
+    n, Hq, Hkv, dh = 50, 4, 2, 16
+    t = qkv_inputs(n, Hq, Hkv, dh, index=0, salt=21)
+    groups = random_groups(n, 6, 2, np.random.default_rng(3))
+    out_s, lse_s = soft_gate_ref(t["q"], t["k"], t["v"], groups, n, 7.0, with_lse=True)
+    out_h, lse_h = attention_rows_ref(t["q"], t["k"], t["v"], groups, n)
+    np.testing.assert_allclose(out_s, out_h, atol=1e-12)
+    np.testing.assert_allclose(lse_s, lse_h, atol=1e-12)
+    # and lse is the log of the softmax normaliser: the weights recomputed from it sum to one
+    _, lse10 = soft_gate_ref(t["q"], t["k"], t["v"], groups, 4, 10.0, with_lse=True)
+    assert lse10.shape == (n, Hq) and np.isfinite(lse10).all()
+    assert (lse10 <= lse_h + 1e-12).all()  # the gate only removes weight (log sigmoid < 0)
