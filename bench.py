@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 
 from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_size,  # noqa: E402
                                         focus_attention, focus_attention_workspace_size,
-                                        focus_bucket, focus_bucket_workspace_size, focus_decode,
+                                        focus_bucket, focus_bucket_append,
+                                        focus_bucket_workspace_size, focus_decode,
                                         focus_soft_attention)
 from learned_centroid_gated_amd import _lib  # noqa: E402
 from synth import CONFIGS, assign_inputs, qkv_inputs, random_groups  # noqa: E402
@@ -350,6 +351,36 @@ def decode_bench(c, steps, warmup):
            "kv_GBs": kv_bytes / (us * 1e-6) / 1e9}
     res["kv_pct_hbm_peak"] = 100 * res["kv_GBs"] / PEAK_HBM_GBS
     log(f"[bench]   decode {us:.1f} us/step, {keys / B:.0f} keys/query, {res['kv_GBs']:.0f} GB/s")
+
+    # membership maintenance per step: the newest token of every cache joins the bucketed
+    # memberships of the others (focus_bucket_append), against bucketing every cache again
+    lens_prev = lens - 1
+    g_prev = cache_groups.clone()
+    g_prev[:, L - 1, :] = -1  # the newest token not yet assigned
+    off_p, idx_p, _ = focus_bucket(g_prev, c.K)
+    new_g = cache_groups[:, L - 1, :].contiguous()
+    off_o, idx_o = torch.empty_like(off_p), torch.empty_like(idx_p)
+
+    def time_us(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(reps):
+            fn()
+        e0.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(e0) * 1e3 / reps
+
+    res["append_us"] = time_us(lambda: focus_bucket_append(new_g, lens, off_p, idx_p, c.K, L,
+                                                           off_o, idx_o))
+    res["rebucket_us"] = time_us(lambda: focus_bucket(cache_groups, c.K))
+    moved = 2 * 4 * float(off_p[:, c.K].sum().item())  # index entries read and written
+    res["append_GBs"] = moved / (res["append_us"] * 1e-6) / 1e9
+    assert torch.equal(off_o, off), "appended offsets differ from the full bucket"
+    del lens_prev, g_prev
+    log(f"[bench]   append {res['append_us']:.1f} us/step ({res['append_GBs']:.0f} GB/s) vs "
+        f"re-bucketing {res['rebucket_us']:.1f} us")
     return res
 
 

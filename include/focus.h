@@ -111,6 +111,30 @@ int focus_bucket(const int32_t* groups, int batch, int64_t n, int K, int top_k,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * focus_bucket_append - one decode step of membership maintenance: token p = cache_len[b] - 1
+ * of every sequence joins the bucketed memberships of tokens 0 .. p - 1 (ZH 2.1.3: it joins
+ * its top-k groups). Its position is the largest so far, so each of its memberships goes at the
+ * end of its group's segment and every segment stays ascending. Given
+ *   offsets_in, idx_in = focus_bucket of tokens 0 .. p - 1 (batch layout [B, K+1], [B, Lmax*top_k]),
+ * it writes offsets_out, idx_out = focus_bucket of tokens 0 .. p, i.e. what focus_decode reads
+ * as cache_offsets / cache_idx; entries of idx_out past offsets_out[b, K] are left unspecified.
+ * Cost: one copy of the index lists (O(p * top_k) bytes per sequence), no sort.
+ *
+ *   new_groups  device, [B, top_k] int32: the new tokens' groups (ids outside [0, K) dropped).
+ *   cache_len   device, [B] int32 in [0, Lmax]: lengths including the new token (0: nothing
+ *               is appended for that sequence).
+ *   B >= 1, Lmax >= 1, 1 <= K <= 1024, 1 <= top_k <= 8.
+ *   offsets_in, idx_in     device, [B, K+1] and [B, Lmax*top_k] int32.
+ *   offsets_out, idx_out   device, same shapes; must not alias the inputs.
+ * Asynchronous on `stream`. The previous state's slot array (focus_bucket's third output) is not
+ * maintained; focus_decode does not read it.
+ * ------------------------------------------------------------------------------------ */
+int focus_bucket_append(const int32_t* new_groups, const int32_t* cache_len, int batch,
+                        int64_t Lmax, int K, int top_k, const int32_t* offsets_in,
+                        const int32_t* idx_in, int32_t* offsets_out, int32_t* idx_out,
+                        void* stream);
+
+/* ------------------------------------------------------------------------------------
  * focus_attention - gated sparse causal attention for one sequence
  * (ZH 2.1.2 and 2.1.3; NL Kerncomponenten 3; ABS).
  *

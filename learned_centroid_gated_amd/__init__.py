@@ -9,6 +9,7 @@ from .focus import (  # noqa: F401
     focus_attention,
     focus_attention_workspace_size,
     focus_bucket,
+    focus_bucket_append,
     focus_bucket_workspace_size,
     focus_decode,
     focus_decode_workspace_size,

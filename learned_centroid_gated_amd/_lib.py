@@ -17,6 +17,7 @@ SIGNATURES = {
                              c_p, c_sz, c_p]),
     "focus_bucket_workspace_size": (c_sz, [c_int, c_i64, c_int, c_int]),
     "focus_bucket": (c_int, [c_p, c_int, c_i64, c_int, c_int, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "focus_bucket_append": (c_int, [c_p, c_p, c_int, c_i64, c_int, c_int, c_p, c_p, c_p, c_p, c_p]),
     "focus_attention_workspace_size": (c_sz, [c_i64, c_int, c_int, c_int, c_int, c_int]),
     "focus_attention": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_p, c_p, c_p,
                                 c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p]),

@@ -178,4 +178,54 @@ hipError_t launch_bucket(const int32_t* groups, int batch, int64_t n, int K, int
   return hipGetLastError();
 }
 
+// ============================================================================ append
+// One new token per sequence joins the bucketed memberships: its position is the largest so
+// far, so each of its memberships goes at the end of its group's segment and every segment
+// keeps ascending positions. Block (g, b) copies segment g of sequence b to its new place
+// (shifted by the new memberships in lower groups) and appends the new token's entries of g.
+__global__ __launch_bounds__(256) void bucket_append_kernel(const int32_t* __restrict__ new_groups,
+                                                            const int32_t* __restrict__ cache_len,
+                                                            int64_t cap, int K, int top_k,
+                                                            const int32_t* __restrict__ off_in,
+                                                            const int32_t* __restrict__ idx_in,
+                                                            int32_t* __restrict__ off_out,
+                                                            int32_t* __restrict__ idx_out) {
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int32_t pos = cache_len[b] - 1;  // the new token (no new token when the cache is empty)
+  int lt = 0, eq = 0, valid = 0;
+  if (pos >= 0) {
+    for (int r = 0; r < top_k; ++r) {
+      const int x = new_groups[(int64_t)b * top_k + r];
+      if (x < 0 || x >= K) continue;  // dropped, as in the bucket sort
+      ++valid;
+      lt += x < g;
+      eq += x == g;
+    }
+  }
+  const int32_t* oi = off_in + (int64_t)b * (K + 1);
+  int32_t* oo = off_out + (int64_t)b * (K + 1);
+  // offsets that do not describe a bucket of at most cap - valid entries are treated as empty
+  // segments, so no access leaves the index lists
+  int32_t s0 = oi[g], s1 = oi[g + 1];
+  if (s0 < 0 || s1 < s0 || (int64_t)s1 + valid > cap) s0 = s1 = 0;
+  const int32_t d0 = s0 + lt;
+  const int32_t* src = idx_in + (int64_t)b * cap;
+  int32_t* dst = idx_out + (int64_t)b * cap;
+  for (int32_t i = t; i < s1 - s0; i += 256) dst[d0 + i] = src[s0 + i];
+  if (t < eq) dst[d0 + (s1 - s0) + t] = pos;
+  if (t == 0) {
+    oo[g] = d0;
+    if (g == K - 1) oo[K] = oi[K] + valid;
+  }
+}
+
+hipError_t launch_bucket_append(const int32_t* new_groups, const int32_t* cache_len, int batch,
+                                int64_t cap, int K, int top_k, const int32_t* off_in,
+                                const int32_t* idx_in, int32_t* off_out, int32_t* idx_out,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(bucket_append_kernel, dim3(K, batch), dim3(256), 0, stream, new_groups,
+                     cache_len, cap, K, top_k, off_in, idx_in, off_out, idx_out);
+  return hipGetLastError();
+}
+
 }  // namespace focus

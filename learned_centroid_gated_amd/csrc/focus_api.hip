@@ -224,6 +224,24 @@ int focus_bucket(const int32_t* groups, int batch, int64_t n, int K, int top_k, 
                                   st));
 }
 
+int focus_bucket_append(const int32_t* new_groups, const int32_t* cache_len, int batch,
+                        int64_t Lmax, int K, int top_k, const int32_t* offsets_in,
+                        const int32_t* idx_in, int32_t* offsets_out, int32_t* idx_out,
+                        void* stream) {
+  if (batch < 1 || Lmax < 1) return FOCUS_ERR_ARG;
+  if (int st = check_groups(K, top_k, 8)) return st;
+  if (Lmax * (int64_t)top_k >= kIdxLimit || (int64_t)batch > 65535) return FOCUS_ERR_SHAPE;
+  if (!new_groups || !cache_len || !offsets_in || !idx_in || !offsets_out || !idx_out)
+    return FOCUS_ERR_ARG;
+  if (offsets_in == offsets_out || idx_in == idx_out) return FOCUS_ERR_ARG;  // out of place
+  if (!aligned4(new_groups) || !aligned4(cache_len) || !aligned4(offsets_in) || !aligned4(idx_in) ||
+      !aligned4(offsets_out) || !aligned4(idx_out))
+    return FOCUS_ERR_ALIGN;
+  return hip_status(launch_bucket_append(new_groups, cache_len, batch, Lmax * top_k, K, top_k,
+                                         offsets_in, idx_in, offsets_out, idx_out,
+                                         (hipStream_t)stream));
+}
+
 // ============================================================================ attention
 size_t focus_attention_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K, int top_k) {
   if (n < 0 || Hq < 1 || Hkv < 1 || d_head < 1 || K < 1 || top_k < 1) return 0;

@@ -127,6 +127,12 @@ hipError_t launch_bucket(const int32_t* groups, int batch, int64_t n, int K, int
                          int32_t* offsets, int32_t* idx, int32_t* slot, int32_t* counts,
                          int32_t* totals, hipStream_t stream);
 
+// Appends one token per sequence to bucketed memberships (out of place; see focus.h).
+hipError_t launch_bucket_append(const int32_t* new_groups, const int32_t* cache_len, int batch,
+                                int64_t cap, int K, int top_k, const int32_t* off_in,
+                                const int32_t* idx_in, int32_t* off_out, int32_t* idx_out,
+                                hipStream_t stream);
+
 // Attention pieces.
 struct AttnShape {
   int64_t n;     // tokens

@@ -122,6 +122,25 @@ def focus_attention(q, k, v, groups, offsets, idx, slot, K, window, scale=0.0, o
     return out, lse
 
 
+# ------------------------------------------------------------------ focus_bucket_append
+def focus_bucket_append(new_groups, cache_len, offsets, idx, K, Lmax, offsets_out=None,
+                        idx_out=None, stream=None):
+    """Token cache_len[b] - 1 of every sequence joins its bucketed memberships: returns
+    (offsets_out [B, K+1], idx_out [B, Lmax * top_k]) from the inputs for the shorter caches."""
+    dev = new_groups.device
+    for t, name in ((new_groups, "new_groups"), (cache_len, "cache_len"), (offsets, "offsets"),
+                    (idx, "idx")):
+        _need(t, name, torch.int32, dev)
+    B, top_k = new_groups.shape
+    if offsets_out is None:
+        offsets_out = torch.empty_like(offsets)
+    if idx_out is None:
+        idx_out = torch.empty_like(idx)
+    _lib_call("focus_bucket_append", _ptr(new_groups), _ptr(cache_len), B, int(Lmax), K, top_k,
+              _ptr(offsets), _ptr(idx), _ptr(offsets_out), _ptr(idx_out), _stream(stream))
+    return offsets_out, idx_out
+
+
 # ------------------------------------------------------------------ focus_soft_attention
 def focus_soft_attention(q, k, v, groups, K, window, lam, scale=0.0, out=None, lse=None,
                          stream=None):

@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -133,6 +133,25 @@ def test_attention_workspace_size(lib):
     # gathered K/V (bf16), fp16 group partials, their log-sum-exp and the key records
     floor = n * k * 2 * Hkv * dh * 2 + n * k * Hq * dh * 2 + n * k * Hq * 4 + n * k * 16
     assert f(n, Hq, Hkv, dh, K, k) >= floor
+
+
+def _append(lib, ng=P, ln=P, B=4, L=1024, K=16, top_k=2, oi=P, ii=P + 65536, oo=P + 4096,
+            io=P + 131072):
+    return lib.focus_bucket_append(ng, ln, B, L, K, top_k, oi, ii, oo, io, None)
+
+
+def test_bucket_append_validation(lib):
+    assert _append(lib, B=0) == ARG
+    assert _append(lib, L=0) == ARG
+    assert _append(lib, K=0) == ARG
+    assert _append(lib, top_k=9, K=16) == UNSUP
+    assert _append(lib, L=1 << 30, top_k=4) == SHAPE
+    assert _append(lib, ng=None) == ARG
+    assert _append(lib, ln=None) == ARG
+    assert _append(lib, oo=P) == ARG          # in place is refused
+    assert _append(lib, io=P + 65536) == ARG
+    assert _append(lib, ln=MIS) == ALIGN
+    assert _append(lib, io=MIS) == ALIGN
 
 
 def _soft(lib, q=P, k=P, v=P, n=256, Hq=8, Hkv=2, dh=128, g=P, K=16, top_k=2, window=32,
