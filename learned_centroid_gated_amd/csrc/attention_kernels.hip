@@ -236,8 +236,10 @@ constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully 
 // SOFT (window pass only): the training-time soft gate instead of the hard pair rule: every
 // causal pair is attended, far pairs with a logit bias that depends on whether the two tokens
 // share a group (the tile's key groups are staged in LDS like the group pass's key records),
-// and there are no group parts to merge.
-template <int DH, bool GROUP, int NLOW, int MKS, bool SOFT = false>
+// and there are no group parts to merge. SMASK (soft gate, T * top_k <= 32): each key of a tile
+// gets a 32-bit mask of the query tokens' group slots (slot c*T + t: group c of token t) that
+// it holds, so the per-element test is one AND with the row's own slots.
+template <int DH, bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   using Smem = FlashSmem<DH, MKS>;
   constexpr int CH = DH / 8;             // 16-byte chunks per key row
@@ -249,8 +251,10 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   static_assert(MKS == 0 || (GROUP && NLOW > 0), "ownership bias only in the group pass");
   static_assert(NLOW >= 0 && NLOW <= 3, "top_k is 1 to 4");
   static_assert(!(SOFT && GROUP), "the soft gate runs on the window pass");
+  static_assert(!SMASK || SOFT, "slot masks belong to the soft gate");
   __shared__ __attribute__((aligned(1024))) Smem smem[2];  // double buffer: one barrier per tile
   __shared__ __attribute__((aligned(16))) int qlow_s[3][32];  // MKS > 0: query tokens' lower groups, -2 if none
+  __shared__ __attribute__((aligned(16))) int qslot_s[SMASK ? 32 : 1];  // SMASK: slot groups, -2 if none
 
   const int tid = threadIdx.x, l = tid & 63, jq = l & 31, hg = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -318,11 +322,13 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
   // soft gate: this row's token's groups (-2 where none or out of range: never matches a key)
   int qg[SOFT ? TK : 1];
+  uint32_t qmask = 0;  // SMASK: this row's token's group slots
   if constexpr (SOFT) {
 #pragma unroll
     for (int c = 0; c < TK; ++c) {
       const int g = qvalid ? a.groups[(int64_t)qi * TK + c] : -2;
       qg[c] = (g >= 0 && g < a.K) ? g : -2;
+      if (SMASK && qg[c] >= 0) qmask |= 1u << (c * a.T + tok_local);
     }
   }
 
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
     gofs[i] = (uint32_t)lrow[i] * kstride_b + gchunk[i];
   }
   i32x4_t ireg = {0x7fffffff, -1, -1, -1};
-  const int kkey = MKS > 0 ? (tid >> 2) : tid;  // key whose record this thread loads
+  const int kkey = (MKS > 0 || SMASK) ? (tid >> 2) : tid;  // key whose record this thread loads
 
   auto issue_tile = [&](int ks, Smem& sb) __attribute__((always_inline)) {
     const char* kb = khead + (int64_t)ks * kstride_b;  // uniform tile base
@@ -489,6 +495,25 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       } else {
         *(i32x4_t*)dst = i32x4_t{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
       }
+    } else if constexpr (SMASK) {
+      // thread (key, quarter tq) matches the key's groups against slots [8 tq, 8 tq + 8); the
+      // quad's four parts are OR-ed on the VALU and kpos holds the key's slot mask
+      const int tq = tid & 3;
+      uint32_t m = 0;
+#pragma unroll
+      for (int u4 = 0; u4 < 2; ++u4) {
+        const i32x4_t qs = *(const i32x4_t*)&qslot_s[8 * tq + 4 * u4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bool hit = false;
+#pragma unroll
+          for (int c = 0; c < TK; ++c) hit = hit || (qs[e] >= 0 && qs[e] == ireg[c]);
+          m |= hit ? 1u << (8 * tq + 4 * u4 + e) : 0u;
+        }
+      }
+      m |= (uint32_t)dpp_move_i<0xB1>((int)m);
+      m |= (uint32_t)dpp_move_i<0x4E>((int)m);
+      if (tq == 0) sb.kpos[kkey] = (int)m;
     } else if constexpr (GROUP || SOFT) {  // soft gate: kpos / klow hold the key's groups
       if (tid < KT) {
         sb.kpos[tid] = ireg[0];
@@ -592,14 +617,20 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
           } else if constexpr (SOFT) {
             // causal; far pairs get the gate's bias, by whether the tokens share a group
             bool share[4] = {false, false, false, false};
+            if constexpr (SMASK) {
+              const i32x4_t km = *(const i32x4_t*)&sm.kpos[kk0];
 #pragma unroll
-            for (int c2 = 0; c2 < TK; ++c2) {
-              const i32x4_t kg = c2 == 0 ? *(const i32x4_t*)&sm.kpos[kk0]
-                                         : *(const i32x4_t*)&sm.klow[c2 > 0 ? c2 - 1 : 0][kk0];
+              for (int e = 0; e < 4; ++e) share[e] = ((uint32_t)km[e] & qmask) != 0u;
+            } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
+              for (int c2 = 0; c2 < TK; ++c2) {
+                const i32x4_t kg = c2 == 0 ? *(const i32x4_t*)&sm.kpos[kk0]
+                                           : *(const i32x4_t*)&sm.klow[c2 > 0 ? c2 - 1 : 0][kk0];
 #pragma unroll
-                for (int c1 = 0; c1 < TK; ++c1) share[e] = share[e] || kg[e] == qg[c1];
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                  for (int c1 = 0; c1 < TK; ++c1) share[e] = share[e] || kg[e] == qg[c1];
+              }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -692,6 +723,18 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       for (int c = 0; c < NLOW; ++c) qlow_s[c][tid] = tok_rec[1 + c] >= 0 ? tok_rec[1 + c] : -2;
     }
     __syncthreads();  // qlow_s is read by every tile's bias rows
+  }
+  if constexpr (SMASK) {
+    if (tid < 32) {  // slot tid: group tid / T of token tid % T (-2 if none or past the tiles)
+      const int c = tid / a.T, tt = tid % a.T;
+      int g = -2;
+      if (c < TK && q0 + tt < q1) {
+        g = a.groups[(int64_t)(q0 + tt) * TK + c];
+        g = (g >= 0 && g < a.K) ? g : -2;
+      }
+      qslot_s[tid] = g;
+    }
+    __syncthreads();  // qslot_s is read by every tile's key masks
   }
   if (ntiles > 0) {
     finish_tile(smem[0]);
@@ -846,14 +889,14 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
 }
 
-template <bool GROUP, int NLOW, int MKS, bool SOFT = false>
+template <bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false>
 static void flash_dispatch_dh(const FlashArgs& fa, int dh, int64_t blocks, hipStream_t stream) {
   if (dh == 128)
-    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS, SOFT>), dim3(blocks), dim3(256), 0,
-                       stream, fa);
+    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS, SOFT, SMASK>), dim3(blocks), dim3(256),
+                       0, stream, fa);
   else
-    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS, SOFT>), dim3(blocks), dim3(256), 0,
-                       stream, fa);
+    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS, SOFT, SMASK>), dim3(blocks), dim3(256),
+                       0, stream, fa);
 }
 
 template <int NLOW>
@@ -961,11 +1004,26 @@ hipError_t launch_soft_attention(const uint16_t* q, const uint16_t* k, const uin
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
   if (blocks <= 0) return hipSuccess;
+  // the group test runs on 32-bit slot masks when the tile's query tokens have at most 32
+  // group slots, else by comparing group ids
+  const bool smask = fa.T * s.top_k <= 32;
   switch (s.top_k) {
-    case 1: flash_dispatch_dh<false, 0, 0, true>(fa, s.dh, blocks, stream); break;
-    case 2: flash_dispatch_dh<false, 1, 0, true>(fa, s.dh, blocks, stream); break;
-    case 3: flash_dispatch_dh<false, 2, 0, true>(fa, s.dh, blocks, stream); break;
-    default: flash_dispatch_dh<false, 3, 0, true>(fa, s.dh, blocks, stream); break;
+    case 1:
+      if (smask) flash_dispatch_dh<false, 0, 0, true, true>(fa, s.dh, blocks, stream);
+      else flash_dispatch_dh<false, 0, 0, true>(fa, s.dh, blocks, stream);
+      break;
+    case 2:
+      if (smask) flash_dispatch_dh<false, 1, 0, true, true>(fa, s.dh, blocks, stream);
+      else flash_dispatch_dh<false, 1, 0, true>(fa, s.dh, blocks, stream);
+      break;
+    case 3:
+      if (smask) flash_dispatch_dh<false, 2, 0, true, true>(fa, s.dh, blocks, stream);
+      else flash_dispatch_dh<false, 2, 0, true>(fa, s.dh, blocks, stream);
+      break;
+    default:
+      if (smask) flash_dispatch_dh<false, 3, 0, true, true>(fa, s.dh, blocks, stream);
+      else flash_dispatch_dh<false, 3, 0, true>(fa, s.dh, blocks, stream);
+      break;
   }
   return hipGetLastError();
 }
