@@ -134,7 +134,7 @@ const char* focus_status_string(int status) {
   }
 }
 
-int focus_version(void) { return 100; }  // 0.1.0
+int focus_version(void) { return 200; }  // 0.2.0: adds focus_bucket_append and focus_soft_attention
 
 // ============================================================================ assign
 size_t focus_assign_workspace_size(int64_t n, int d, int d_g, int K) {
