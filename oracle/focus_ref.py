@@ -30,6 +30,10 @@ What the pages fix, and the reading taken where they are silent:
   * Exact softmax over the allowed pairs (NL Kerncomponenten 3), each allowed pair once.
     Reading: scale 1/sqrt(d_head); lse is the natural log of the sum of exp(scaled logits).
   * GQA (NL Belangrijkste Bijdragen 3; ZH 3.2): query head h reads kv head h // (Hq/Hkv).
+  * Asymmetric top-k (NL Resultaten, "Inferentie": each token looks at 2 of the 4 groups for
+    a 2x speed-up; ZH 4 table, top-k trade-off): reading used: every key sits in its top-1
+    group only, a query looks at its k groups, and a far pair is allowed when the key's group
+    is one of the query's. This is what makes "2 of 4 groups" halve the far pairs.
   * Soft gate (ZH 2.1.2 formula): the printed form multiplies the logit by the gate, which
     cannot approach a hard mask; reading used: the gate multiplies the weight exp(q.k),
     i.e. adds log(sigmoid(lambda * a_ij)) to the logit of far pairs, with group affinity
@@ -235,6 +239,65 @@ def decode_ref(q, q_groups, k_cache, v_cache, cache_len, cache_groups, window, s
         l = _logsumexp(s, axis=1)
         out[b] = np.einsum("hj,jhd->hd", np.exp(s - l[:, None]), vj)
         lse[b] = l
+    return out, lse
+
+
+# ------------------------------------------------------------------ asymmetric top-k variant
+def allowed_keys_asym_ref(i, q_groups, k_group, window):
+    """Keys j that query i may attend under the asymmetric top-k reading (NL Resultaten,
+    "Inferentie"; ZH 4 table): j <= i and (i - j < window or k_group[j] is one of the
+    query's groups q_groups[i]). k_group [n] is each token's single key group (its top-1),
+    q_groups [n, k] the groups each token looks at as a query.
+    """
+    looked_at = np.asarray(q_groups)[i]
+    j = np.arange(i + 1)
+    local = (i - j) < window
+    far_ok = np.isin(np.asarray(k_group).reshape(-1)[:i + 1], looked_at)
+    return j[local | far_ok]
+
+
+def pair_count_asym_ref(q_groups, k_group, window):
+    """Exact allowed-key count of every query under the asymmetric rule, [n] int64:
+    min(i + 1, window) plus, for each distinct group g the query looks at, the number of keys
+    j <= i - window whose key group is g (one ascending position list per group, searched).
+    """
+    q_groups = np.asarray(q_groups, np.int64)
+    k_group = np.asarray(k_group, np.int64).reshape(-1)
+    n = q_groups.shape[0]
+    pos = np.arange(n, dtype=np.int64)
+    counts = np.minimum(pos + 1, window).astype(np.int64)
+    members = {int(g): pos[k_group == g] for g in np.unique(k_group)}
+    for i in range(n):
+        limit = i - window
+        if limit < 0:
+            continue
+        for g in set(int(x) for x in q_groups[i]):
+            if g in members:
+                counts[i] += int(np.searchsorted(members[g], limit, side="right"))
+    return counts
+
+
+def attention_rows_asym_ref(q, k, v, q_groups, k_group, window, scale=None, rows=None):
+    """Exact masked softmax attention under the asymmetric top-k rule for the given query rows
+    (NL Kerncomponenten 3 with the pair set of allowed_keys_asym_ref). Shapes and outputs as
+    attention_rows_ref: (out [len(rows), Hq, dh], lse [len(rows), Hq]) in fp64.
+    """
+    n, Hq, dh = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(dh) if scale is None or scale <= 0 else float(scale)
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    kv_of = np.arange(Hq) // G
+    out = np.empty((len(rows), Hq, v.shape[2]))
+    lse = np.empty((len(rows), Hq))
+    for r, i in enumerate(rows):
+        J = allowed_keys_asym_ref(int(i), q_groups, k_group, window)
+        qi = _widen(q[i])
+        kj = _widen(k[J])[:, kv_of, :]
+        vj = _widen(v[J])[:, kv_of, :]
+        s = scale * np.einsum("hd,jhd->hj", qi, kj)
+        l = _logsumexp(s, axis=1)
+        out[r] = np.einsum("hj,jhd->hd", np.exp(s - l[:, None]), vj)
+        lse[r] = l
     return out, lse
 
 
