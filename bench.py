@@ -5,7 +5,8 @@ A step is one pass of the prefill hot path over one synthetic sequence with ever
 resident in HBM: focus_assign (scores, Sinkhorn, top-k) -> focus_bucket -> focus_attention
 (gather, group pass, window pass with the merge in its epilogue). The headline line is the
 128K-token 70B-shaped GQA layer; the 1M-token prefill, the batched decode, a dense causal
-baseline on the same GPU and the training-time soft-gate forward are reported beside it. Kernel
+baseline on the same GPU, the training-time soft-gate forward and the asymmetric top-k variant
+(keys in their top-1 group) are reported beside it. Kernel
 times inside focus_attention come from HIP events the library records on its own stream around
 each stage (focus_attention_ex).
 
@@ -26,7 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_size,  # noqa: E402
-                                        focus_attention, focus_attention_workspace_size,
+                                        focus_attention, focus_attention_asym,
+                                        focus_attention_asym_workspace_size,
+                                        focus_attention_workspace_size,
                                         focus_bucket, focus_bucket_append,
                                         focus_bucket_workspace_size, focus_decode,
                                         focus_soft_attention)
@@ -247,8 +250,11 @@ def prefill_bench(c, steps, warmup, hip):
                            "algorithmic_per_launch": gather_bytes, "avg_launch_ms": stage_ms[dom]}
     log(f"[bench]   {ms:.3f} ms/step  {res['tokens_per_s']:.4g} tok/s  stages {stage_ms} "
         f"assign {assign_ms:.3f} bucket {bucket_ms:.3f}")
-    state = dict(q=q, k=k, v=v, groups=groups, off=off, idx=idx, slot=slot, out=out, lse=lse,
-                 ws_t=ws_t)
+    # each token's top-1 group from the same assignment (the key side of the asymmetric variant)
+    groups1 = torch.empty((c.n, 1), dtype=torch.int32, device=dev)
+    focus_assign(hidden, w_g, cents, 1, c.iters, groups=groups1, workspace=ws_a)
+    state = dict(q=q, k=k, v=v, groups=groups, groups1=groups1, off=off, idx=idx, slot=slot,
+                 out=out, lse=lse, ws_t=ws_t)
     del hidden, w_g, cents, a, t, ws_a, ws_b
     return res, state
 
@@ -304,6 +310,59 @@ def dense_baseline(c, st, hip, reps=2):
         del qt, kt, vt
     except Exception as ex:  # report, do not fail the bench
         res["torch_sdpa_causal_error"] = f"{type(ex).__name__}: {str(ex)[:160]}"
+    return res
+
+
+# ------------------------------------------------------------------ asymmetric top-k
+def asym_bench(c, st, dense_ms, sym_attn_ms, reps=3):
+    """focus_attention_asym on the same Q/K/V: keys in their top-1 group, queries looking at
+    top_k groups. Two memberships: the library's own assignment at K groups (query groups =
+    the step's top-2, key group = top-1 of the same scores), and the pages' 2-of-4 setting with
+    synthetic balanced memberships (4 groups, each token looking at 2, its key group one of
+    them). Times the attention call (gather, plan, group pass, window pass with the merge)."""
+    q, k, v, out, lse = st["q"], st["k"], st["v"], st["out"], st["lse"]
+    dev = q.device
+    rng = np.random.default_rng(c.index + 4)
+    g4 = random_groups(c.n, 4, 2, rng)
+    k4 = g4[np.arange(c.n), rng.integers(0, 2, size=c.n)]
+    cases = {
+        f"K{c.K}_top{c.top_k}_assigned": (c.K, st["groups"], st["groups1"]),
+        "K4_top2_two_of_four": (4, torch.from_numpy(g4).to(dev),
+                                torch.from_numpy(k4.astype(np.int32)[:, None].copy()).to(dev)),
+    }
+    flops_pair = 4.0 * c.dh * c.Hq
+    res = {}
+    for name, (K, qg, kg) in cases.items():
+        qb = focus_bucket(qg, K)
+        kb = focus_bucket(kg, K)
+        ws = torch.empty(focus_attention_asym_workspace_size(c.n, c.Hq, c.Hkv, c.dh, K,
+                                                             qg.shape[1]),
+                         dtype=torch.uint8, device=dev)
+        times = []
+        for r in range(reps + 1):
+            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            focus_attention_asym(q, k, v, qb, kb, K, c.window, out=out, lse=lse, workspace=ws)
+            e0.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(s0.elapsed_time(e0))
+        ms = float(np.mean(times))
+        # exact allowed pairs from a Q = 0 run: exp(lse_i) counts row i's keys
+        q0 = torch.zeros_like(q)
+        _, l0 = focus_attention_asym(q0, k, v, qb, kb, K, c.window, workspace=ws)
+        pairs = int(torch.exp(l0[:, 0].double()).round().to(torch.int64).sum().item())
+        del q0, l0, ws
+        torch.cuda.empty_cache()
+        r = {"attention_ms": ms, "allowed_pairs": pairs,
+             "density_vs_causal": pairs / (c.n * (c.n + 1) / 2),
+             "attention_tflops": flops_pair * pairs / (ms * 1e-3) / 1e12,
+             "speedup_vs_own_dense": dense_ms / ms if dense_ms else None}
+        if K == c.K:
+            r["symmetric_attention_ms"] = sym_attn_ms
+        log(f"[bench] asym {name}: {ms:.3f} ms, density {r['density_vs_causal']:.4f}, "
+            f"{r['attention_tflops']:.0f} TFLOP/s")
+        res[name] = r
     return res
 
 
@@ -458,6 +517,9 @@ def main():
         extra["dense_baseline_128k"] = dense_baseline(c3, st3, hip)
         extra["dense_baseline_128k"]["focus_speedup_vs_own_dense"] = (
             extra["dense_baseline_128k"]["own_window_kernel_ms"] / res3["ms_per_step"])
+        sym_attn = sum(res3["attention_stage_ms"].values())
+        extra["asym_128k"] = asym_bench(c3, st3, extra["dense_baseline_128k"]["own_window_kernel_ms"],
+                                        sym_attn)
     del st3
     torch.cuda.empty_cache()
     if not args.quick:

@@ -181,6 +181,38 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        void* const* stage_events, int num_events);
 
 /* ------------------------------------------------------------------------------------
+ * focus_attention_asym - the asymmetric top-k reading of top-k inference (Dutch summary,
+ * Resultaten, "Inferentie": each token looks at 2 of the 4 groups for a 2x speed-up; Chinese
+ * summary, section 4 table, top-k trade-off). Every token sits, as a key, in one group k_group
+ * (its top-1: focus_assign with top_k 1) and looks, as a query, at its top_k groups q_groups
+ * (focus_assign with top_k):
+ *
+ *   allowed(i, j) = j <= i and (i - j < window or k_group[j] is one of q_groups[i])
+ *
+ * and out / lse are as for focus_attention over that pair set. A far pair meets exactly one of
+ * the query's memberships (the key has one group), so no ownership rule is needed; the window
+ * pass merges the top_k group parts by log-sum-exp as in focus_attention.
+ *
+ *   q, k, v, n, Hq, Hkv, d_head, K, window, scale, out, lse   as for focus_attention
+ *            (window 0 with k_group[i] not among q_groups[i] leaves row i with no pairs:
+ *            lse -inf, out 0).
+ *   q_offsets, q_idx, q_slot   device, focus_bucket output for q_groups [n, top_k] (batch 1).
+ *   top_k    1 <= top_k <= min(K, 4), groups each query looks at.
+ *   k_offsets, k_idx, k_slot   device, focus_bucket output for k_group [n, 1] (batch 1).
+ *   workspace  at least focus_attention_asym_workspace_size(n, Hq, Hkv, d_head, K, top_k)
+ *            bytes. Errors as for focus_attention; asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------ */
+size_t focus_attention_asym_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K,
+                                           int top_k);
+int focus_attention_asym(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         int64_t n, int Hq, int Hkv, int d_head,
+                         const int32_t* q_offsets, const int32_t* q_idx, const int32_t* q_slot,
+                         int top_k,
+                         const int32_t* k_offsets, const int32_t* k_idx, const int32_t* k_slot,
+                         int K, int64_t window, float scale, uint16_t* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * focus_soft_attention - the training-time soft gate (ZH 2.1.2 gate formula), forward only:
  * exact softmax over every causal pair, with far pairs' weights multiplied by the gate
  * sigmoid(lambda * a_ij):

@@ -7,6 +7,8 @@ from .focus import (  # noqa: F401
     focus_assign,
     focus_assign_workspace_size,
     focus_attention,
+    focus_attention_asym,
+    focus_attention_asym_workspace_size,
     focus_attention_workspace_size,
     focus_bucket,
     focus_bucket_append,

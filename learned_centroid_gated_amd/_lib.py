@@ -24,6 +24,10 @@ SIGNATURES = {
     "focus_attention_ex": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_p, c_p, c_p,
                                    c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p,
                                    ctypes.POINTER(c_p), c_int]),
+    "focus_attention_asym_workspace_size": (c_sz, [c_i64, c_int, c_int, c_int, c_int, c_int]),
+    "focus_attention_asym": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_p, c_p,
+                                     c_int, c_p, c_p, c_p, c_int, c_i64, c_f, c_p, c_p, c_p,
+                                     c_sz, c_p]),
     "focus_soft_attention": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_int, c_int,
                                      c_i64, c_f, c_f, c_p, c_p, c_p]),
     "focus_decode_workspace_size": (c_sz, [c_int, c_i64, c_int, c_int, c_int, c_int, c_int]),

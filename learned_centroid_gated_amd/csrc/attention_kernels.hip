@@ -170,6 +170,54 @@ hipError_t launch_plan_tiles(const int32_t* offsets, const int32_t* tile_pre, co
   return hipGetLastError();
 }
 
+// Asymmetric top-k: plan[item] = (q0, q1, kv_lo, kv_hi) with query slots [q0, q1) of the
+// query bucket's segment g and key slots [kv_lo, kv_hi] of the key bucket's segment g: the keys
+// of group g at positions up to the tile's last query position minus the window, the only ones
+// with a far pair in the item (kv_hi = kv_lo - 1: none). Items in the same order as above.
+__global__ __launch_bounds__(256) void plan_tiles_asym_kernel(
+    const int32_t* __restrict__ q_off, const int32_t* __restrict__ tile_pre,
+    const int32_t* __restrict__ q_idx, const int32_t* __restrict__ k_off,
+    const int32_t* __restrict__ k_idx, int K, int T, int window, int w_max,
+    i32x4_t* __restrict__ plan) {
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= w_max) return;
+  i32x4_t p = {0, 0, 0, -1};
+  if (item < tile_pre[K]) {
+    int lo = 0, hi = K - 1;  // largest g with tile_pre[g] <= item (a non-empty segment)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_pre[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    const int nt = tile_pre[lo + 1] - tile_pre[lo];
+    const int t = nt - 1 - (item - tile_pre[lo]);
+    const int q0 = q_off[lo] + t * T, q1 = min(q0 + T, q_off[lo + 1]);
+    const int limit = q_idx[q1 - 1] - window;  // far keys sit at positions <= limit
+    int a = k_off[lo], b = k_off[lo + 1];       // first key slot past the limit, in [a, b]
+    const int kv_lo = a;
+    while (a < b) {
+      const int mid = (a + b) >> 1;
+      if (k_idx[mid] <= limit) a = mid + 1;
+      else b = mid;
+    }
+    p = i32x4_t{q0, q1, kv_lo, a - 1};
+  }
+  plan[item] = p;
+}
+
+hipError_t launch_plan_tiles_asym(const int32_t* q_off, const int32_t* tile_pre,
+                                  const int32_t* q_idx, const int32_t* k_off,
+                                  const int32_t* k_idx, const AttnShape& s, int32_t* plan,
+                                  hipStream_t stream) {
+  const int T = attn_tile_tokens(s.G);
+  const int w_max = attn_work_items(s.nk, T, s.K);
+  const int window = (int)(s.window < s.n ? s.window : s.n);
+  hipLaunchKernelGGL(plan_tiles_asym_kernel, dim3((w_max + 255) / 256), dim3(256), 0, stream,
+                     q_off, tile_pre, q_idx, k_off, k_idx, s.K, T, window, w_max,
+                     (i32x4_t*)plan);
+  return hipGetLastError();
+}
+
 // ============================================================================ flash kernel
 struct FlashArgs {
   const uint16_t* q;  // [n, Hq, DH] in token order (group pass: row of slot s is kinfo[s].x)
@@ -188,10 +236,12 @@ struct FlashArgs {
   const int32_t* seg_off;   // group: [K+1]
   const int32_t* tile_pre;  // group: [K+1]
   const i32x4_t* kinfo;     // group: per slot (position, lower groups, -1 padded)
-  const i32x4_t* plan;      // group: per work item (q0, q1, kv_lo, ntiles); q0 == q1: none
+  const i32x4_t* plan;      // group: per work item (q0, q1, kv_lo, ntiles), asymmetric
+                            // (q0, q1, kv_lo, kv_hi); q0 == q1: none
   int w_max;                // group: work items per kv head (upper bound)
   int K;
   int tiles_per_head;       // window: ceil(n / T)
+  const int32_t* qidx;      // asymmetric group pass: query slot -> token position
   const int32_t* groups;    // soft gate: [n, top_k] memberships
   float soft_b0, soft_b1;   // soft gate: far-pair logit bias without / with a shared group,
                             // in raw q.k units (log sigmoid(lambda * (share - 1/2)) / scale)
@@ -239,7 +289,13 @@ constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully 
 // and there are no group parts to merge. SMASK (soft gate, T * top_k <= 32): each key of a tile
 // gets a 32-bit mask of the query tokens' group slots (slot c*T + t: group c of token t) that
 // it holds, so the per-element test is one AND with the row's own slots.
-template <int DH, bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false>
+// ASYM (group pass, asymmetric top-k): query slots come from the bucket of the groups each
+// token looks at and key slots from a second bucket in which every token sits in one group,
+// so the two slot spaces differ: query positions come from qidx, the plan gives each item's
+// key range, tile classes compare positions only, and no ownership rule is needed (a key has
+// one group, so each far pair meets exactly one of the query's memberships).
+template <int DH, bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false,
+          bool ASYM = false>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   using Smem = FlashSmem<DH, MKS>;
   constexpr int CH = DH / 8;             // 16-byte chunks per key row
@@ -252,6 +308,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   static_assert(NLOW >= 0 && NLOW <= 3, "top_k is 1 to 4");
   static_assert(!(SOFT && GROUP), "the soft gate runs on the window pass");
   static_assert(!SMASK || SOFT, "slot masks belong to the soft gate");
+  static_assert(!ASYM || (GROUP && NLOW == 0 && MKS == 0), "asymmetric: group pass, one key group");
   __shared__ __attribute__((aligned(1024))) Smem smem[2];  // double buffer: one barrier per tile
   __shared__ __attribute__((aligned(16))) int qlow_s[3][32];  // MKS > 0: query tokens' lower groups, -2 if none
   __shared__ __attribute__((aligned(16))) int qslot_s[SMASK ? 32 : 1];  // SMASK: slot groups, -2 if none
@@ -267,20 +324,26 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   const int item = (int)(comb - (int64_t)h * W);
   const int window = a.window;
 
-  int q0, q1, kv_lo, ntiles;  // slots (group) or tokens (window); all below 2^31
+  int q0, q1, kv_lo, kv_hi, ntiles;  // slots (group) or tokens (window); all below 2^31
   if constexpr (GROUP) {
     const i32x4_t pl = a.plan[item];  // one load replaces the searches of the work item
     q0 = pl[0];
     q1 = pl[1];
     kv_lo = pl[2];
-    ntiles = pl[3];
+    if constexpr (ASYM) {
+      kv_hi = pl[3];
+      ntiles = kv_hi >= kv_lo ? (kv_hi - kv_lo) / KT + 1 : 0;
+    } else {
+      kv_hi = q1 - 1;  // last key slot any query of the tile may see
+      ntiles = pl[3];
+    }
     if (q0 >= q1) return;
   } else {
     q0 = item * a.T;
     q1 = (int)min((int64_t)q0 + a.T, a.n);
     kv_lo = SOFT ? 0 : max(q0 - window + 1, 0);
+    kv_hi = q1 - 1;  // last key index any query of the tile may see
   }
-  const int kv_hi = q1 - 1;  // last key index any query of the tile may see
 
   // ---------------------------------------------------------------- this lane's query row
   const int r = wave * 32 + jq;
@@ -296,7 +359,13 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
   int qpos = 0, wpos_lo = 0, wpos_hi = 0;
   int qlow[3] = {-2, -2, -2};
-  if constexpr (GROUP) {
+  if constexpr (ASYM) {
+    if (qvalid) qpos = a.qidx[qi];
+    if (wave_active) {
+      wpos_lo = a.qidx[wq_lo];
+      wpos_hi = a.qidx[wq_hi];
+    }
+  } else if constexpr (GROUP) {
     if (qvalid) {
       i32x4_t qinfo = a.kinfo[qi];
       qpos = qinfo[0];
@@ -532,10 +601,16 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       const bool whole = k_last <= kv_hi;
       const int kp_first = __builtin_amdgcn_readfirstlane(sm.kpos[0]);
       const int kp_last = whole ? __builtin_amdgcn_readfirstlane(sm.kpos[KT - 1]) : 0x7fffffff;
-      if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
-      else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
-        cls = (NLOW == 0 || MKS > 0) ? kFull : kFar;
-      else cls = kEdge;
+      if constexpr (ASYM) {  // key and query slots are separate: positions decide
+        if (wpos_hi - kp_first < window) cls = kSkip;
+        else if (whole && wpos_lo - kp_last >= window) cls = kFull;
+        else cls = kEdge;
+      } else {
+        if (ks > wq_hi || wpos_hi - kp_first < window) cls = kSkip;
+        else if (whole && k_last <= wq_lo && wpos_lo - kp_last >= window)
+          cls = (NLOW == 0 || MKS > 0) ? kFull : kFar;
+        else cls = kEdge;
+      }
     } else {
       if (ks > wq_hi || (!SOFT && wq_lo - k_last >= window)) cls = kSkip;
       else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
@@ -889,14 +964,14 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
 }
 
-template <bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false>
+template <bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false, bool ASYM = false>
 static void flash_dispatch_dh(const FlashArgs& fa, int dh, int64_t blocks, hipStream_t stream) {
   if (dh == 128)
-    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS, SOFT, SMASK>), dim3(blocks), dim3(256),
-                       0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<128, GROUP, NLOW, MKS, SOFT, SMASK, ASYM>), dim3(blocks),
+                       dim3(256), 0, stream, fa);
   else
-    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS, SOFT, SMASK>), dim3(blocks), dim3(256),
-                       0, stream, fa);
+    hipLaunchKernelGGL((flash_kernel<64, GROUP, NLOW, MKS, SOFT, SMASK, ASYM>), dim3(blocks),
+                       dim3(256), 0, stream, fa);
 }
 
 template <int NLOW>
@@ -943,6 +1018,35 @@ hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const u
     case 3: flash_dispatch_group<2>(fa, s.dh, mks, blocks, stream); break;
     default: flash_dispatch_group<3>(fa, s.dh, mks, blocks, stream); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_group_attention_asym(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
+                                       const int32_t* q_idx, const int32_t* kinfo,
+                                       const int32_t* plan, const AttnShape& s, _Float16* og,
+                                       float* lseg, hipStream_t stream) {
+  FlashArgs fa{};
+  fa.q = q;
+  fa.k = kg;
+  fa.v = vg;
+  fa.og = og;
+  fa.lseg = lseg;
+  fa.n = s.n;
+  fa.Hq = s.Hq;
+  fa.Hkv = s.Hkv;
+  fa.G = s.G;
+  fa.T = attn_tile_tokens(s.G);
+  fa.window = (int)(s.window < s.n ? s.window : s.n);
+  fa.sl2 = s.scale * kLog2e;
+  fa.kinfo = (const i32x4_t*)kinfo;
+  fa.qidx = q_idx;
+  fa.plan = (const i32x4_t*)plan;
+  fa.K = s.K;
+  fa.top_k = s.top_k;
+  fa.w_max = attn_work_items(s.nk, fa.T, s.K);
+  const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.w_max);
+  if (blocks <= 0) return hipSuccess;
+  flash_dispatch_dh<true, 0, 0, false, false, true>(fa, s.dh, blocks, stream);
   return hipGetLastError();
 }
 

@@ -97,6 +97,26 @@ size_t attn_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k
   return c.used;
 }
 
+// Asymmetric top-k: K/V gathered along the key bucket (one entry per token) with its key
+// records, the group pass's partials per query membership, the tile prefix and the plan.
+size_t attn_asym_carve(void* ws, int64_t n, int Hq, int Hkv, int dh, int K, int top_k,
+                       AttnWs* out) {
+  Carver c(ws);
+  const int64_t nq = n * top_k;
+  AttnWs w{};
+  w.kg = c.take<uint16_t>((size_t)n * Hkv * dh);
+  w.vg = c.take<uint16_t>((size_t)n * Hkv * dh);
+  w.og = c.take<_Float16>((size_t)nq * Hq * dh);
+  w.lseg = c.take<float>((size_t)nq * Hq);
+  w.kinfo = c.take<int32_t>((size_t)n * 4);
+  w.tile_pre = c.take<int32_t>((size_t)K + 1);
+  const int G = Hq / Hkv > 1 ? Hq / Hkv : 1;
+  const int T = attn_tile_tokens(G) > 1 ? attn_tile_tokens(G) : 1;
+  w.plan = c.take<int32_t>((size_t)4 * attn_work_items(nq, T, K));
+  if (out) *out = w;
+  return c.used;
+}
+
 int check_heads(int Hq, int Hkv, int d_head) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FOCUS_ERR_ARG;
   if (!is_pow2_upto16(Hq / Hkv)) return FOCUS_ERR_UNSUPPORTED;
@@ -134,7 +154,7 @@ const char* focus_status_string(int status) {
   }
 }
 
-int focus_version(void) { return 200; }  // 0.2.0: adds focus_bucket_append and focus_soft_attention
+int focus_version(void) { return 300; }  // 0.3.0: adds focus_attention_asym
 
 // ============================================================================ assign
 size_t focus_assign_workspace_size(int64_t n, int d, int d_g, int K) {
@@ -304,6 +324,62 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   if (e == hipSuccess)
     e = launch_window_attention(q, k, v, w.og, w.lseg, slot, s, out, lse, st);
   if (e == hipSuccess) e = mark(7);
+  return hip_status(e);
+}
+
+size_t focus_attention_asym_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K,
+                                           int top_k) {
+  if (n < 0 || Hq < 1 || Hkv < 1 || d_head < 1 || K < 1 || top_k < 1) return 0;
+  return attn_asym_carve(nullptr, n, Hq, Hkv, d_head, K, top_k, nullptr);
+}
+
+int focus_attention_asym(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
+                         int Hq, int Hkv, int d_head, const int32_t* q_offsets,
+                         const int32_t* q_idx, const int32_t* q_slot, int top_k,
+                         const int32_t* k_offsets, const int32_t* k_idx, const int32_t* k_slot,
+                         int K, int64_t window, float scale, uint16_t* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || window < 0) return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  if (n * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (n == 0) return FOCUS_OK;
+  if (!q || !k || !v || !q_offsets || !q_idx || !q_slot || !k_offsets || !k_idx || !k_slot ||
+      !out || !lse)
+    return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(q_offsets) ||
+      !aligned4(q_idx) || !aligned4(q_slot) || !aligned4(k_offsets) || !aligned4(k_idx) ||
+      !aligned4(k_slot) || !aligned16(out) || !aligned4(lse) || !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  AttnWs w;
+  const size_t need = attn_asym_carve(workspace, n, Hq, Hkv, d_head, K, top_k, &w);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+
+  AttnShape s{};  // query side: n * top_k memberships
+  s.n = n;
+  s.nk = n * top_k;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
+  s.K = K;
+  s.top_k = top_k;
+  s.window = window < n + 1 ? window : n + 1;
+  s.scale = sc;
+  AttnShape sk = s;  // key side: one membership per token
+  sk.nk = n;
+  sk.top_k = 1;
+  hipStream_t st = (hipStream_t)stream;
+  // with one group per token the gather reads no group list (a key has no lower groups)
+  hipError_t e = launch_gather_kv(k, v, k_idx, nullptr, k_slot, sk, w.kg, w.vg, w.kinfo, st);
+  if (e == hipSuccess) e = launch_tile_prefix(q_offsets, K, attn_tile_tokens(s.G), w.tile_pre, st);
+  if (e == hipSuccess)
+    e = launch_plan_tiles_asym(q_offsets, w.tile_pre, q_idx, k_offsets, k_idx, s, w.plan, st);
+  if (e == hipSuccess)
+    e = launch_group_attention_asym(q, w.kg, w.vg, q_idx, w.kinfo, w.plan, s, w.og, w.lseg, st);
+  if (e == hipSuccess) e = launch_window_attention(q, k, v, w.og, w.lseg, q_slot, s, out, lse, st);
   return hip_status(e);
 }
 

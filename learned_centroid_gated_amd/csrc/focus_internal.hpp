@@ -154,6 +154,18 @@ hipError_t launch_group_attention(const uint16_t* q, const uint16_t* kg, const u
                                   const int32_t* offsets, const int32_t* tile_pre,
                                   const int32_t* kinfo, const int32_t* plan, const AttnShape& s,
                                   _Float16* og, float* lseg, hipStream_t stream);
+// Asymmetric top-k (s.nk = query memberships, s.top_k = groups per query): the work plan from
+// the query bucket (q_off, q_idx, tile prefix over q_off) and the key bucket (k_off, k_idx), and
+// the group pass over keys gathered along the key bucket (kinfo from launch_gather_kv with
+// top_k 1). The window pass is launch_window_attention with the query slots.
+hipError_t launch_plan_tiles_asym(const int32_t* q_off, const int32_t* tile_pre,
+                                  const int32_t* q_idx, const int32_t* k_off,
+                                  const int32_t* k_idx, const AttnShape& s, int32_t* plan,
+                                  hipStream_t stream);
+hipError_t launch_group_attention_asym(const uint16_t* q, const uint16_t* kg, const uint16_t* vg,
+                                       const int32_t* q_idx, const int32_t* kinfo,
+                                       const int32_t* plan, const AttnShape& s, _Float16* og,
+                                       float* lseg, hipStream_t stream);
 hipError_t launch_window_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    const _Float16* og, const float* lseg, const int32_t* slot,
                                    const AttnShape& s, uint16_t* out, float* lse,

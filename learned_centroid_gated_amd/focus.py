@@ -122,6 +122,41 @@ def focus_attention(q, k, v, groups, offsets, idx, slot, K, window, scale=0.0, o
     return out, lse
 
 
+# ------------------------------------------------------------------ focus_attention_asym
+def focus_attention_asym_workspace_size(n, Hq, Hkv, d_head, K, top_k):
+    return _lib.lib().focus_attention_asym_workspace_size(n, Hq, Hkv, d_head, K, top_k)
+
+
+def focus_attention_asym(q, k, v, q_bucket, k_bucket, K, window, scale=0.0, out=None, lse=None,
+                         workspace=None, stream=None):
+    """Asymmetric top-k gated attention: q_bucket = focus_bucket(q_groups [n, top_k]) for the
+    groups each token looks at, k_bucket = focus_bucket(k_group [n, 1]) for each token's single
+    key group. Returns (out [n, Hq, dh] bf16, lse [n, Hq] fp32)."""
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, dev)
+    q_off, q_idx, q_slot = q_bucket
+    k_off, k_idx, k_slot = k_bucket
+    for t, name in ((q_off, "q_offsets"), (q_idx, "q_idx"), (q_slot, "q_slot"),
+                    (k_off, "k_offsets"), (k_idx, "k_idx"), (k_slot, "k_slot")):
+        _need(t, name, torch.int32, dev)
+    n, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    top_k = q_slot.shape[-1]
+    if k_slot.shape[-1] != 1:
+        raise ValueError("k_bucket must come from one key group per token")
+    if out is None:
+        out = torch.empty((n, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((n, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_attention_asym_workspace_size(n, Hq, Hkv, dh, K, top_k), dev, workspace)
+    _lib_call("focus_attention_asym", _ptr(q), _ptr(k), _ptr(v), n, Hq, Hkv, dh, _ptr(q_off),
+              _ptr(q_idx), _ptr(q_slot), top_k, _ptr(k_off), _ptr(k_idx), _ptr(k_slot), K,
+              int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(stream))
+    return out, lse
+
+
 # ------------------------------------------------------------------ focus_bucket_append
 def focus_bucket_append(new_groups, cache_len, offsets, idx, K, Lmax, offsets_out=None,
                         idx_out=None, stream=None):

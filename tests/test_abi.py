@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -178,6 +178,35 @@ def test_soft_attention_validation(lib):
     assert _soft(lib, k=MIS) == ALIGN
     assert _soft(lib, out=MIS) == ALIGN
     assert _soft(lib, n=0, q=None) == OK  # empty: nothing enqueued
+
+
+def _asym(lib, q=P, k=P, v=P, n=256, Hq=8, Hkv=2, dh=128, qo=P, qi=P, qs=P, top_k=2, ko=P, ki=P,
+          ks=P, K=16, window=64, scale=0.0, out=P, lse=P, ws=P, wsb=BIG):
+    return lib.focus_attention_asym(q, k, v, n, Hq, Hkv, dh, qo, qi, qs, top_k, ko, ki, ks, K,
+                                    window, scale, out, lse, ws, wsb, None)
+
+
+def test_attention_asym_validation(lib):
+    assert _asym(lib, n=-1) == ARG
+    assert _asym(lib, window=-1) == ARG
+    assert _asym(lib, scale=math.nan) == ARG
+    assert _asym(lib, Hq=6, Hkv=4) == ARG
+    assert _asym(lib, Hq=6, Hkv=2) == UNSUP
+    assert _asym(lib, dh=96) == UNSUP
+    assert _asym(lib, K=0) == ARG
+    assert _asym(lib, top_k=5, K=16) == UNSUP
+    assert _asym(lib, n=1 << 30, top_k=2) == SHAPE
+    for name in ("q", "qo", "qi", "qs", "ko", "ki", "ks", "out", "lse"):
+        assert _asym(lib, **{name: None}) == ARG, name
+    assert _asym(lib, v=MIS) == ALIGN
+    assert _asym(lib, ki=P + 2) == ALIGN
+    assert _asym(lib, ws=None) == WS
+    assert _asym(lib, wsb=16) == WS
+    assert _asym(lib, n=0, q=None) == OK  # empty: nothing enqueued
+    small = lib.focus_attention_asym_workspace_size(1000, 8, 2, 128, 16, 2)
+    sym = lib.focus_attention_workspace_size(1000, 8, 2, 128, 16, 2)
+    assert 0 < small < sym  # K/V gathered once per token, not once per membership
+    assert lib.focus_attention_asym_workspace_size(-1, 8, 2, 128, 16, 2) == 0
 
 
 def _decode(lib, q=P, qg=P, kc=P, vc=P, ln=P, cg=P, co=P, ci=P, B=4, L=1024, Hq=8, Hkv=2, dh=128,
