@@ -32,6 +32,7 @@ from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_siz
                                         focus_attention_workspace_size,
                                         focus_bucket, focus_bucket_append,
                                         focus_bucket_workspace_size, focus_decode,
+                                        focus_decode_paged,
                                         focus_soft_attention)
 from learned_centroid_gated_amd import _lib  # noqa: E402
 from synth import CONFIGS, assign_inputs, qkv_inputs, random_groups  # noqa: E402
@@ -410,6 +411,41 @@ def decode_bench(c, steps, warmup):
            "kv_GBs": kv_bytes / (us * 1e-6) / 1e9}
     res["kv_pct_hbm_peak"] = 100 * res["kv_GBs"] / PEAK_HBM_GBS
     log(f"[bench]   decode {us:.1f} us/step, {keys / B:.0f} keys/query, {res['kv_GBs']:.0f} GB/s")
+    out_ref = out.clone()
+    focus_decode(qd, q_groups, t["k"], t["v"], lens, cache_groups, off, idx, c.K, c.window,
+                 out=out_ref, lse=lse)
+
+    # the same step over a paged cache: 16-token pages scattered through one pool in a seeded
+    # random order (focus_decode_paged), checked equal to the unpaged step
+    page = 16
+    pps = L // page
+    perm = torch.from_numpy(np.random.default_rng(c.index).permutation(B * pps)).to(dev)
+    kp = torch.empty((B * pps, page, c.Hkv, c.dh), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    kp[perm] = t["k"].reshape(B * pps, page, c.Hkv, c.dh)
+    vp[perm] = t["v"].reshape(B * pps, page, c.Hkv, c.dh)
+    table = perm.to(torch.int32).reshape(B, pps).contiguous()
+
+    def step_paged():
+        focus_decode_paged(qd, q_groups, kp, vp, table, lens, cache_groups, off, idx, c.K,
+                           c.window, out=out, lse=lse)
+
+    step_paged()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16)), "paged decode differs"
+    for _ in range(warmup):
+        step_paged()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        step_paged()
+    e.record()
+    torch.cuda.synchronize()
+    res["paged16_us_per_step"] = s.elapsed_time(e) * 1e3 / steps
+    res["paged16_kv_GBs"] = kv_bytes / (res["paged16_us_per_step"] * 1e-6) / 1e9
+    log(f"[bench]   paged decode (16-token pages) {res['paged16_us_per_step']:.1f} us/step, "
+        f"{res['paged16_kv_GBs']:.0f} GB/s")
+    del kp, vp, perm, table, out_ref
 
     # membership maintenance per step: the newest token of every cache joins the bucketed
     # memberships of the others (focus_bucket_append), against bucketing every cache again

@@ -270,6 +270,35 @@ int focus_decode(const uint16_t* q, const int32_t* q_groups,
                  uint16_t* out, float* lse,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * focus_decode_paged - focus_decode over a paged KV cache (the paged cache that goes with
+ * incremental decode; Chinese summary, section 2.1.3 inference). The K/V rows of all
+ * sequences live in one pool of fixed-size pages; each sequence lists its pages in order.
+ * Position p of sequence b is pool row page_table[b, p / page_size] * page_size +
+ * p % page_size. Results equal focus_decode on the caches the pages spell out (same keys,
+ * same order, same arithmetic).
+ *
+ *   k_pages, v_pages  device, [num_pages, page_size, Hkv, d_head] bf16.
+ *   num_pages >= 1, page_size >= 1, num_pages * page_size <= 2^31 (pool rows are int32).
+ *   page_table   device, [B, pages_per_seq] int32 page ids. Only the pages that hold
+ *                positions < cache_len[b] are read; keys on an entry outside
+ *                [0, num_pages) are skipped (never read).
+ *   pages_per_seq >= 1; Lmax = pages_per_seq * page_size is the logical capacity:
+ *                cache_groups [B, Lmax, top_k], cache_offsets / cache_idx from focus_bucket
+ *                over them (batch B, n = Lmax), cache_len[b] <= Lmax.
+ *   Other arguments, limits, workspace (focus_decode_workspace_size(B, Lmax, ...)) and
+ *   errors as for focus_decode.
+ * ------------------------------------------------------------------------------------ */
+int focus_decode_paged(const uint16_t* q, const int32_t* q_groups,
+                       const uint16_t* k_pages, const uint16_t* v_pages,
+                       int64_t num_pages, int page_size,
+                       const int32_t* page_table, int64_t pages_per_seq,
+                       const int32_t* cache_len, const int32_t* cache_groups,
+                       const int32_t* cache_offsets, const int32_t* cache_idx,
+                       int B, int Hq, int Hkv, int d_head, int K, int top_k,
+                       int64_t window, float scale, uint16_t* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,9 @@ SIGNATURES = {
     "focus_soft_attention": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_int, c_int,
                                      c_i64, c_f, c_f, c_p, c_p, c_p]),
     "focus_decode_workspace_size": (c_sz, [c_int, c_i64, c_int, c_int, c_int, c_int, c_int]),
+    "focus_decode_paged": (c_int, [c_p, c_p, c_p, c_p, c_i64, c_int, c_p, c_i64, c_p, c_p, c_p,
+                                   c_p, c_int, c_int, c_int, c_int, c_int, c_int, c_i64, c_f,
+                                   c_p, c_p, c_p, c_sz, c_p]),
     "focus_decode": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int, c_int,
                              c_int, c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p]),
 }

@@ -87,12 +87,17 @@ __global__ __launch_bounds__(64) void decode_seg_kernel(const int32_t* __restric
 
 // list[b][vi] = key position of virtual list entry vi, or -1 when the entry is a member of a
 // query group that a lower shared query group owns (so every allowed key is listed once).
+// With a page table the entry is the key's row in the shared page pool instead:
+// table[b][pos / page] * page + pos % page, or -1 when the table entry is not a page of the pool.
 __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restrict__ q_groups,
                                                           const int32_t* __restrict__ cache_groups,
                                                           const int32_t* __restrict__ cache_idx,
                                                           const int32_t* __restrict__ info,
                                                           int64_t Lmax, int K, int top_k,
                                                           int64_t per_seq,
+                                                          const int32_t* __restrict__ table,
+                                                          int page, int64_t pages_per_seq,
+                                                          int64_t num_pages,
                                                           int32_t* __restrict__ list) {
   const int b = (int)(blockIdx.x / kListBlocks);
   const int32_t* inf = info + (int64_t)b * kDecInfo;
@@ -126,6 +131,10 @@ __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restr
         rem -= cnt;
       }
     }
+    if (table && pos >= 0) {
+      const int64_t pg = table[(int64_t)b * pages_per_seq + pos / page];
+      pos = (pg >= 0 && pg < num_pages) ? (int)(pg * page + pos % page) : -1;
+    }
     list[(int64_t)b * per_seq + vi] = pos;
   }
 }
@@ -138,7 +147,7 @@ struct DecodeArgs {
   const int32_t* list;
   int64_t per_seq;  // list capacity per sequence
   int B;
-  int64_t Lmax;
+  int64_t seq_rows;  // rows between consecutive sequences' caches (0: list rows are pool rows)
   int Hq, Hkv, G, top_k, splits;
   int hpb;  // query heads per unit (<= kDecHeads), all of one kv head
   int upb;  // units per block: divides the block's lane groups and the units of a sequence
@@ -231,8 +240,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   }
 
   const int64_t kv_stride = (int64_t)a.Hkv * DH;
-  const uint16_t* kbase = a.kc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
-  const uint16_t* vbase = a.vc + (int64_t)b * a.Lmax * kv_stride + (int64_t)h * DH + c * 8;
+  const uint16_t* kbase = a.kc + (int64_t)b * a.seq_rows * kv_stride + (int64_t)h * DH + c * 8;
+  const uint16_t* vbase = a.vc + (int64_t)b * a.seq_rows * kv_stride + (int64_t)h * DH + c * 8;
 
   // entries v0 + slot + k * slots of the piece, U at a time
   int pn[U];
@@ -395,7 +404,7 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
                          int32_t* info, int32_t* list, float* part_o, float* part_ml,
-                         uint16_t* out, float* lse, hipStream_t stream) {
+                         uint16_t* out, float* lse, hipStream_t stream, const DecodePaging* pg) {
   const int64_t per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
   hipLaunchKernelGGL(decode_seg_kernel, dim3((int64_t)s.B * s.top_k), dim3(64), 0, stream,
                      q_groups, cache_len, cache_off, cache_idx, s.Lmax, s.K, s.top_k, s.window,
@@ -404,7 +413,8 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   if (s.splits != kDecSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * kListBlocks), dim3(256),
                      0, stream, q_groups, cache_groups, cache_idx, info, s.Lmax, s.K, s.top_k,
-                     per_seq, list);
+                     per_seq, pg ? pg->table : nullptr, pg ? pg->page_size : 1,
+                     pg ? pg->pages_per_seq : 0, pg ? pg->num_pages : 0, list);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   DecodeArgs a{};
   a.q = q;
@@ -414,7 +424,7 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   a.list = list;
   a.per_seq = per_seq;
   a.B = s.B;
-  a.Lmax = s.Lmax;
+  a.seq_rows = pg ? 0 : s.Lmax;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.G = s.G;

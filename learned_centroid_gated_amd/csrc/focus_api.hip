@@ -154,7 +154,7 @@ const char* focus_status_string(int status) {
   }
 }
 
-int focus_version(void) { return 300; }  // 0.3.0: adds focus_attention_asym
+int focus_version(void) { return 400; }  // 0.4.0: adds focus_decode_paged
 
 // ============================================================================ assign
 size_t focus_assign_workspace_size(int64_t n, int d, int d_g, int K) {
@@ -494,6 +494,55 @@ int focus_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_c
   return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
                                   cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
                                   w.part_ml, out, lse, (hipStream_t)stream));
+}
+
+int focus_decode_paged(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_pages,
+                       const uint16_t* v_pages, int64_t num_pages, int page_size,
+                       const int32_t* page_table, int64_t pages_per_seq, const int32_t* cache_len,
+                       const int32_t* cache_groups, const int32_t* cache_offsets,
+                       const int32_t* cache_idx, int B, int Hq, int Hkv, int d_head, int K,
+                       int top_k, int64_t window, float scale, uint16_t* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || window < 0 || num_pages < 1 || page_size < 1 || pages_per_seq < 1)
+    return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  // pool rows and logical positions are kept as 32-bit ints
+  if (num_pages > kIdxLimit / page_size || pages_per_seq > kIdxLimit / page_size)
+    return FOCUS_ERR_SHAPE;
+  const int64_t Lmax = pages_per_seq * page_size;
+  if (Lmax * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (B == 0) return FOCUS_OK;
+  if (!q || !q_groups || !k_pages || !v_pages || !page_table || !cache_len || !cache_groups ||
+      !cache_offsets || !cache_idx || !out || !lse)
+    return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned4(q_groups) || !aligned16(k_pages) || !aligned16(v_pages) ||
+      !aligned4(page_table) || !aligned4(cache_len) || !aligned4(cache_groups) ||
+      !aligned4(cache_offsets) || !aligned4(cache_idx) || !aligned16(out) || !aligned4(lse) ||
+      !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  const size_t need = focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+  DecodeShape s{};
+  s.B = B;
+  s.Lmax = Lmax;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
+  s.K = K;
+  s.top_k = top_k;
+  s.window = window;
+  s.scale = sc;
+  s.splits = decode_splits(s);
+  DecodeWs w;
+  decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  DecodePaging pg{page_table, page_size, pages_per_seq, num_pages};
+  return hip_status(launch_decode(q, q_groups, k_pages, v_pages, cache_len, cache_groups,
+                                  cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
+                                  w.part_ml, out, lse, (hipStream_t)stream, &pg));
 }
 
 }  // extern "C"

@@ -187,10 +187,19 @@ struct DecodeShape {
   int splits;  // key-range splits per (sequence, kv head)
 };
 int decode_splits(const DecodeShape& s);
+// Paged caches: kc / vc are pools of num_pages pages of page_size token rows; position p of
+// sequence b lives in row table[b * pages_per_seq + p / page_size] * page_size + p % page_size.
+struct DecodePaging {
+  const int32_t* table;
+  int page_size;
+  int64_t pages_per_seq, num_pages;
+};
+// pg == nullptr: kc / vc are [B, Lmax, Hkv, dh] per-sequence caches.
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
                          int32_t* info, int32_t* list, float* part_o, float* part_ml,
-                         uint16_t* out, float* lse, hipStream_t stream);
+                         uint16_t* out, float* lse, hipStream_t stream,
+                         const DecodePaging* pg = nullptr);
 
 }  // namespace focus

@@ -225,3 +225,34 @@ def focus_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups, cache_o
               Hq, Hkv, dh, K, top_k, int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
               ws.numel() * ws.element_size(), _stream(stream))
     return out, lse
+
+
+def focus_decode_paged(q, q_groups, k_pages, v_pages, page_table, cache_len, cache_groups,
+                       cache_offsets, cache_idx, K, window, scale=0.0, out=None, lse=None,
+                       workspace=None, stream=None):
+    """focus_decode over a paged cache: k_pages / v_pages [num_pages, page_size, Hkv, dh] bf16,
+    page_table [B, pages_per_seq] int32; cache_groups [B, pages_per_seq * page_size, top_k].
+    Returns (out [B, Hq, dh] bf16, lse [B, Hq])."""
+    dev = q.device
+    for t, name in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, name, torch.bfloat16, dev)
+    for t, name in ((q_groups, "q_groups"), (page_table, "page_table"), (cache_len, "cache_len"),
+                    (cache_groups, "cache_groups"), (cache_offsets, "cache_offsets"),
+                    (cache_idx, "cache_idx")):
+        _need(t, name, torch.int32, dev)
+    B, Hq, dh = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    pages_per_seq = page_table.shape[1]
+    Lmax = pages_per_seq * page_size
+    top_k = q_groups.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_decode_workspace_size(B, Lmax, Hq, Hkv, dh, K, top_k), dev, workspace)
+    _lib_call("focus_decode_paged", _ptr(q), _ptr(q_groups), _ptr(k_pages), _ptr(v_pages),
+              num_pages, page_size, _ptr(page_table), pages_per_seq, _ptr(cache_len),
+              _ptr(cache_groups), _ptr(cache_offsets), _ptr(cache_idx), B, Hq, Hkv, dh, K, top_k,
+              int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(stream))
+    return out, lse

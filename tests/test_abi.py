@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -233,3 +233,30 @@ def test_python_binding_refuses_host_tensors():
     from learned_centroid_gated_amd import focus_assign
     with pytest.raises(ValueError, match="device tensor"):
         focus_assign(torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(2, 4), 1, 1)
+
+
+def _paged(lib, q=P, qg=P, kp=P, vp=P, npages=64, page=16, table=P, pps=8, ln=P, cg=P, co=P,
+           ci=P, B=4, Hq=8, Hkv=2, dh=128, K=16, top_k=2, window=64, scale=0.0, out=P, lse=P,
+           ws=P, wsb=BIG):
+    return lib.focus_decode_paged(q, qg, kp, vp, npages, page, table, pps, ln, cg, co, ci, B, Hq,
+                                  Hkv, dh, K, top_k, window, scale, out, lse, ws, wsb, None)
+
+
+def test_decode_paged_validation(lib):
+    assert _paged(lib, B=-1) == ARG
+    assert _paged(lib, npages=0) == ARG
+    assert _paged(lib, page=0) == ARG
+    assert _paged(lib, pps=0) == ARG
+    assert _paged(lib, window=-1) == ARG
+    assert _paged(lib, dh=32) == UNSUP
+    assert _paged(lib, top_k=5, K=16) == UNSUP
+    assert _paged(lib, npages=(1 << 27) + 1, page=16) == SHAPE  # pool rows past 2^31
+    assert _paged(lib, pps=1 << 27, page=16) == SHAPE
+    assert _paged(lib, pps=1 << 26, page=16, top_k=2) == SHAPE  # Lmax * top_k past 2^31
+    for name in ("q", "qg", "kp", "vp", "table", "ln", "cg", "co", "ci", "out", "lse"):
+        assert _paged(lib, **{name: None}) == ARG, name
+    assert _paged(lib, kp=MIS) == ALIGN
+    assert _paged(lib, table=P + 2) == ALIGN
+    assert _paged(lib, ws=None) == WS
+    assert _paged(lib, wsb=16) == WS
+    assert _paged(lib, B=0, q=None) == OK
