@@ -280,7 +280,8 @@ def pair_count_asym_ref(q_groups, k_group, window):
 def attention_rows_asym_ref(q, k, v, q_groups, k_group, window, scale=None, rows=None):
     """Exact masked softmax attention under the asymmetric top-k rule for the given query rows
     (NL Kerncomponenten 3 with the pair set of allowed_keys_asym_ref). Shapes and outputs as
-    attention_rows_ref: (out [len(rows), Hq, dh], lse [len(rows), Hq]) in fp64.
+    attention_rows_ref: (out [len(rows), Hq, dh], lse [len(rows), Hq]) in fp64. A row with no
+    allowed key (possible only at window 0) has lse -inf and out 0.
     """
     n, Hq, dh = q.shape
     G = Hq // k.shape[1]
@@ -291,6 +292,9 @@ def attention_rows_asym_ref(q, k, v, q_groups, k_group, window, scale=None, rows
     lse = np.empty((len(rows), Hq))
     for r, i in enumerate(rows):
         J = allowed_keys_asym_ref(int(i), q_groups, k_group, window)
+        if len(J) == 0:  # window 0 and the token's key group outside its query groups
+            out[r], lse[r] = 0.0, -np.inf
+            continue
         qi = _widen(q[i])
         kj = _widen(k[J])[:, kv_of, :]
         vj = _widen(v[J])[:, kv_of, :]

@@ -52,6 +52,7 @@ CASES = [
     (3000, 32, 8, 128, 256, 3, 512, 0, True),
     (1500, 8, 8, 64, 5, 4, 33, 0.7, True),
     (1700, 16, 4, 128, 12, 2, 50, 0, False),
+    (3000, 16, 1, 64, 1024, 4, 100, 0, True),   # largest K and top_k, G = 16
     (800, 8, 2, 64, 4, 3, 1, 0, False),
 ]
 
@@ -66,6 +67,27 @@ def test_asym_matches_oracle(n, Hq, Hkv, dh, K, k, w, skew, inside):
                         i32_dev(kg), K, w)
     o_ref, l_ref = attention_rows_asym_ref(t["q"], t["k"], t["v"], qg, kg, w)
     check_attention(out, lse, o_ref, l_ref, f"asym n={n} K={K} k={k} w={w}")
+
+
+def test_asym_rows_without_allowed_keys():
+    """Window 0 with key groups drawn apart from the query groups: rows whose key group is not
+    among their own query groups and that meet no earlier key of their groups have no pair at
+    all; they must come out with lse -inf and out 0, and every other row as the oracle."""
+    n, Hq, Hkv, dh, K, k = 900, 8, 2, 128, 6, 1
+    say(f"asym empty rows n={n} K={K} top_k={k} window=0")
+    t = qkv_inputs(n, Hq, Hkv, dh, index=0, salt=77)
+    qg, kg = asym_groups(n, K, k, 77, inside=False)
+    out, lse = run_asym(bf16_dev(t["q"]), bf16_dev(t["k"]), bf16_dev(t["v"]), i32_dev(qg),
+                        i32_dev(kg), K, 0)
+    o_ref, l_ref = attention_rows_asym_ref(t["q"], t["k"], t["v"], qg, kg, 0)
+    empty = ~np.isfinite(l_ref[:, 0])
+    say(f"  rows without keys: {int(empty.sum())}")
+    assert empty.any() and not empty.all()
+    lse_h, out_h = to_np(lse), to_np(out)
+    assert np.all(lse_h[empty] == -np.inf)
+    assert np.all(out_h[empty] == 0)
+    keep = torch.from_numpy(np.nonzero(~empty)[0]).cuda()
+    check_attention(out[keep], lse[keep], o_ref[~empty], l_ref[~empty], "asym window 0, non-empty rows")
 
 
 def test_asym_custom_scale():

@@ -160,3 +160,22 @@ def test_assigned_top1_lies_in_assigned_topk():
     a1 = assign_ref(inp["hidden"], inp["w_g"], inp["centroids"], 1, 3)["groups"][:, 0]
     a3 = assign_ref(inp["hidden"], inp["w_g"], inp["centroids"], 3, 3)["groups"]
     assert all(a1[i] in a3[i] for i in range(n))
+
+
+def test_row_without_allowed_keys_has_lse_minus_infinity():
+    """Window 0 and a key group outside the token's own query groups: token 1 (key group 1,
+    looking at group 0) has no earlier key of group 0 and does not see itself."""
+    qg = np.array([[0], [0], [1]], np.int32)
+    kg = np.array([0, 1, 1], np.int32)
+    assert list(allowed_keys_asym_ref(1, qg, kg, 0)) == [0]
+    assert list(allowed_keys_asym_ref(0, qg, kg, 0)) == [0]
+    qg2 = np.array([[1], [0], [1]], np.int32)  # token 0 looks at group 1, its key group is 0
+    assert len(allowed_keys_asym_ref(0, qg2, kg, 0)) == 0
+    q = np.random.default_rng(1).normal(size=(3, 2, 4))
+    k = np.random.default_rng(2).normal(size=(3, 1, 4))
+    v = np.random.default_rng(3).normal(size=(3, 1, 4))
+    out, lse = attention_rows_asym_ref(q, k, v, qg2, kg, 0)
+    assert np.all(lse[0] == -np.inf) and np.all(out[0] == 0)
+    assert pair_count_asym_ref(qg2, kg, 0)[0] == 0
+    # row 2 (looks at group 1) sees keys 1 and 2: an ordinary softmax
+    assert np.isfinite(lse[2]).all()
