@@ -245,6 +245,7 @@ struct FlashArgs {
   const int32_t* groups;    // soft gate: [n, top_k] memberships
   float soft_b0, soft_b1;   // soft gate: far-pair logit bias without / with a shared group,
                             // in raw q.k units (log sigmoid(lambda * (share - 1/2)) / scale)
+  float soft_shift;         // soft gate with bias rows: soft_b0 in natural-log units
 };
 
 constexpr int KT = 64;  // keys per kv tile
@@ -297,14 +298,16 @@ constexpr float kMaskFloor = -0x1p99f;   // raw row maxima below this are fully 
 template <int DH, bool GROUP, int NLOW, int MKS, bool SOFT = false, bool SMASK = false,
           bool ASYM = false>
 __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
-  using Smem = FlashSmem<DH, MKS>;
+  using Smem = FlashSmem<DH, (SOFT && MKS > 0) ? 1 : MKS>;  // soft gate: one share row block
   constexpr int CH = DH / 8;             // 16-byte chunks per key row
   constexpr int ROWS_PER_INST = 64 / CH; // key rows one wave-wide 1 KB LDS load covers
   constexpr int INSTS = KT / ROWS_PER_INST / 4;  // per wave, for each of K and V
   constexpr int NS = DH / 16;            // MFMA k-steps over the head dimension
   constexpr int ND = DH / 32;            // 32-wide output tiles over the head dimension
   constexpr int RB = 2 * DH;             // bytes per key row
-  static_assert(MKS == 0 || (GROUP && NLOW > 0), "ownership bias only in the group pass");
+  static_assert(MKS == 0 || (GROUP && NLOW > 0) || (SOFT && SMASK && MKS == 3),
+                "bias rows: the group pass's ownership rule, or the soft gate's share term");
+  constexpr bool SBIAS = SOFT && MKS > 0;  // soft gate: far-pair share term on the MFMA
   static_assert(NLOW >= 0 && NLOW <= 3, "top_k is 1 to 4");
   static_assert(!(SOFT && GROUP), "the soft gate runs on the window pass");
   static_assert(!SMASK || SOFT, "slot masks belong to the soft gate");
@@ -412,7 +415,26 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
   // query side of the ownership bias: -2^100 at this row's token (T <= 32: token = jq % T)
   bf16x8_t qm[MKS > 0 ? MKS : 1];
-  if constexpr (MKS > 0) {
+  // soft gate with bias rows: logits are shifted by -soft_b0 for every pair of a row (lse adds
+  // it back), so far pairs need only c = soft_b1 - soft_b0 times share. The MFMA adds it as the
+  // three bf16 parts of c (8 + 8 + 8 significand bits hold all of fp32, so the sum is c
+  // exactly), one k-step each over the same share rows
+  float soft_c = 0.f;
+  if constexpr (SBIAS) {
+    const float c = a.soft_b1 - a.soft_b0;
+    const __bf16 c0 = to_bf16(c);
+    const __bf16 c1 = to_bf16(c - (float)c0);
+    const __bf16 c2 = to_bf16(c - (float)c0 - (float)c1);
+    soft_c = c;
+    const int tw = jq % a.T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool hit = 8 * hg + e == tw;
+      qm[0][e] = hit ? c0 : (__bf16)0.f;
+      qm[1][e] = hit ? c1 : (__bf16)0.f;
+      qm[2][e] = hit ? c2 : (__bf16)0.f;
+    }
+  } else if constexpr (MKS > 0) {
     const int tw = jq % a.T;
 #pragma unroll
     for (int j = 0; j < MKS; ++j)
@@ -421,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
   // the tile's query tokens' records (for the lower-group table written after the first wait)
   i32x4_t tok_rec = {0, -2, -2, -2};
-  if constexpr (MKS > 0) {
+  if constexpr (GROUP && MKS > 0) {
     if (tid < 32 && tid < a.T && q0 + tid < q1) tok_rec = a.kinfo[q0 + tid];
   }
 
@@ -583,6 +605,21 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       m |= (uint32_t)dpp_move_i<0xB1>((int)m);
       m |= (uint32_t)dpp_move_i<0x4E>((int)m);
       if (tq == 0) sb.kpos[kkey] = (int)m;
+      if constexpr (SBIAS) {
+        // share rows (T <= 16): thread tq writes tokens [4 tq, 4 tq + 4) of the key's row;
+        // entries of tokens past T are never selected by a row's one-hot
+        uint32_t w2[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * tq + e;
+          uint32_t tm = 0;  // slots of token t
+#pragma unroll
+          for (int c = 0; c < TK; ++c) tm |= (t < a.T && c * a.T + t < 32) ? 1u << (c * a.T + t) : 0u;
+          w2[e >> 1] |= (m & tm) ? (0x3F80u << (16 * (e & 1))) : 0u;
+        }
+        const i32x2_t wv = {(int)w2[0], (int)w2[1]};
+        *(i32x2_t*)&sb.mrow[0][kkey][4 * tq] = wv;
+      }
     } else if constexpr (GROUP || SOFT) {  // soft gate: kpos / klow hold the key's groups
       if (tid < KT) {
         sb.kpos[tid] = ireg[0];
@@ -611,6 +648,10 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
           cls = (NLOW == 0 || MKS > 0) ? kFull : kFar;
         else cls = kEdge;
       }
+    } else if constexpr (SBIAS) {
+      if (ks > wq_hi) cls = kSkip;
+      else if (wq_lo - k_last >= window) cls = kFull;  // all pairs far and causal: rows only
+      else cls = kEdge;
     } else {
       if (ks > wq_hi || (!SOFT && wq_lo - k_last >= window)) cls = kSkip;
       else if (k_last <= wq_lo && wq_hi - ks < window) cls = kFull;
@@ -620,7 +661,15 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
     // ------------------------------------------------------------ S^T = K Q^T (+ bias)
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-    if constexpr (MKS > 0) {
+    if constexpr (SBIAS) {  // one share row block, one k-step per part of c
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t mf = *(const bf16x8_t*)(lds + mrd + par + kb * 32 * 32);
+#pragma unroll
+        for (int j = 0; j < MKS; ++j)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, qm[j], sacc[kb], 0, 0, 0);
+      }
+    } else if constexpr (MKS > 0) {
 #pragma unroll
       for (int j = 0; j < MKS; ++j)
 #pragma unroll
@@ -711,7 +760,11 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
             for (int e = 0; e < 4; ++e) {
               const int dd = qi - (ks + kk0 + e);
               ok[e] = dd >= 0;
-              if (dd >= window) sacc[kb][4 * q4 + e] += share[e] ? a.soft_b1 : a.soft_b0;
+              if constexpr (SBIAS) {  // near pairs: undo the share term, take the row shift
+                if (dd < window) sacc[kb][4 * q4 + e] -= a.soft_b0 + (share[e] ? soft_c : 0.f);
+              } else {
+                if (dd >= window) sacc[kb][4 * q4 + e] += share[e] ? a.soft_b1 : a.soft_b0;
+              }
             }
           } else {
 #pragma unroll
@@ -732,7 +785,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 #pragma unroll
       for (int vi = 0; vi < 16; ++vi) mx[2 * kb + (vi >> 3)] = fmaxf(mx[2 * kb + (vi >> 3)], sacc[kb][vi]);
     float tmax = pair32_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-    if constexpr (MKS > 0) tmax = tmax < kMaskFloor ? -INFINITY : tmax;
+    if constexpr (GROUP && MKS > 0) tmax = tmax < kMaskFloor ? -INFINITY : tmax;
     tmax *= a.sl2;
     // Lazy rescale: the reference max moves only when a row's max exceeds it by more than
     // kLazy (log2 units), so p = exp2(x - m_ref) stays below 2^kLazy and O is rescaled on
@@ -792,7 +845,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
   }
   if (ntiles > 0) issue_tile(kv_lo, smem[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if constexpr (MKS > 0) {
+  if constexpr (GROUP && MKS > 0) {
     if (tid < 32) {
 #pragma unroll
       for (int c = 0; c < NLOW; ++c) qlow_s[c][tid] = tok_rec[1 + c] >= 0 ? tok_rec[1 + c] : -2;
@@ -960,7 +1013,9 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
         }
       }
     }
-    if (qvalid && hg == 0) a.lse[(int64_t)qi * a.Hq + hq] = den > 0.f ? M + __logf(den) : -INFINITY;
+    if (qvalid && hg == 0)
+      a.lse[(int64_t)qi * a.Hq + hq] =
+          den > 0.f ? M + __logf(den) + (SBIAS ? a.soft_shift : 0.f) : -INFINITY;
   }
 }
 
@@ -1105,12 +1160,24 @@ hipError_t launch_soft_attention(const uint16_t* q, const uint16_t* k, const uin
   fa.sl2 = s.scale * kLog2e;
   fa.soft_b0 = bias_none / s.scale;
   fa.soft_b1 = bias_share / s.scale;
+  fa.soft_shift = bias_none;
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
   if (blocks <= 0) return hipSuccess;
   // the group test runs on 32-bit slot masks when the tile's query tokens have at most 32
   // group slots, else by comparing group ids
   const bool smask = fa.T * s.top_k <= 32;
+  // with at most 16 query tokens per tile the far pairs' share term runs as three MFMA bias
+  // k-steps and only tiles that reach the window or the diagonal keep per-element work
+  if (smask && fa.T <= 16) {
+    switch (s.top_k) {
+      case 1: flash_dispatch_dh<false, 0, 3, true, true>(fa, s.dh, blocks, stream); break;
+      case 2: flash_dispatch_dh<false, 1, 3, true, true>(fa, s.dh, blocks, stream); break;
+      case 3: flash_dispatch_dh<false, 2, 3, true, true>(fa, s.dh, blocks, stream); break;
+      default: flash_dispatch_dh<false, 3, 3, true, true>(fa, s.dh, blocks, stream); break;
+    }
+    return hipGetLastError();
+  }
   switch (s.top_k) {
     case 1:
       if (smask) flash_dispatch_dh<false, 0, 0, true, true>(fa, s.dh, blocks, stream);

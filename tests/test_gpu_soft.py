@@ -24,6 +24,14 @@ CASES = [
     (513, 2, 1, 128, 3, 3, 700, 2.0),
     (300, 8, 8, 64, 4, 4, 64, 50.0),
     (777, 8, 1, 128, 12, 2, 100, -3.0),
+    # G >= 8 (at most 16 query tokens per tile): the share term on the MFMA bias rows
+    (1000, 16, 2, 128, 16, 2, 0, 4.0),
+    (2049, 16, 2, 128, 128, 2, 1024, 10.0),
+    (900, 16, 1, 64, 7, 4, 1, 6.0),
+    (700, 32, 2, 128, 9, 3, 700, 2.0),
+    (1300, 8, 1, 64, 5, 1, 37, -8.0),
+    (640, 16, 2, 128, 6, 2, 64, 60.0),
+    (520, 16, 2, 128, 6, 2, 40, 1000.0),  # the share term's parts must add up to it exactly
 ]
 
 
@@ -40,9 +48,10 @@ def test_soft_matches_oracle(n, Hq, Hkv, dh, K, k, w, lam):
     check_attention(out, lse, o_ref, l_ref, "soft")
 
 
-def test_soft_large_lambda_reaches_hard_rule():
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (16, 2)])
+def test_soft_large_lambda_reaches_hard_rule(Hq, Hkv):
     from learned_centroid_gated_amd import focus_attention, focus_bucket, focus_soft_attention
-    n, Hq, Hkv, dh, K, k, w = 1500, 8, 2, 128, 16, 2, 64
+    n, dh, K, k, w = 1500, 128, 16, 2, 64
     t = qkv_inputs(n, Hq, Hkv, dh, index=0, salt=77)
     groups = random_groups(n, K, k, np.random.default_rng(5))
     q, kk, v, g = bf16_dev(t["q"]), bf16_dev(t["k"]), bf16_dev(t["v"]), i32_dev(groups)
