@@ -7,11 +7,12 @@
 // sees itself), then for each query group g_r the segment members at positions <= p - w'
 // whose lowest group shared with the query is g_r, so every allowed key appears once.
 //
-// Three steps. A plan kernel finds, per sequence, the window and each query group's slice of
-// its bucketed memberships; a list kernel resolves the virtual list into key positions once per
-// sequence (-1 for members that a lower shared group owns). The partial kernel cuts each list
-// into `splits` pieces; its blocks read every listed key's K and V rows, all kv heads of a
-// token at once where the head count allows, and keep a running (max, sum, O) per query head.
+// Three steps. A list kernel finds, per sequence, the window and each query group's slice of
+// its bucketed memberships (the plan), then resolves the virtual list into key positions once
+// per sequence (-1 for members that a lower shared query group owns). The partial kernel cuts
+// each list into `splits` pieces; its blocks read every listed key's K and V rows, all kv heads
+// of a token at once where the head count allows, and keep a running (max, sum, O) per query
+// head.
 // A combine kernel merges the pieces by log-sum-exp. The path is HBM-bound: every allowed key
 // costs one K row and one V row per kv head.
 #include "focus_internal.hpp"
@@ -31,32 +32,14 @@ int decode_splits(const DecodeShape& s) {
 // ============================================================================ plan
 // info[b] = (lo, nl, 0, seg_lo_0, cnt_0, ..., seg_lo_3, cnt_3): the window is positions
 // lo .. lo + nl - 1; query group r contributes the cnt_r members of its segment from index
-// seg_lo_r on, those at positions <= p - w'. One wave per (sequence, query group) finds the
-// boundary with a 64-ary search: each step probes 64 evenly spaced members at once.
-__global__ __launch_bounds__(64) void decode_seg_kernel(const int32_t* __restrict__ q_groups,
-                                                        const int32_t* __restrict__ cache_len,
-                                                        const int32_t* __restrict__ cache_off,
-                                                        const int32_t* __restrict__ cache_idx,
-                                                        int64_t Lmax, int K, int top_k,
-                                                        int64_t window,
-                                                        int32_t* __restrict__ info) {
-  const int b = blockIdx.x / top_k, r = blockIdx.x % top_k, l = threadIdx.x;
-  int64_t L = cache_len[b];
-  if (L < 1) L = 1;
-  if (L > Lmax) L = Lmax;
-  const int64_t p = L - 1;
-  const int64_t wl = window > 1 ? window : 1;
-  const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
-  int32_t* inf = info + (int64_t)b * kDecInfo;
-  if (r == 0 && l == 0) {
-    inf[0] = (int32_t)lo;
-    inf[1] = (int32_t)(p - lo + 1);
-    inf[2] = 0;
-    for (int rr = top_k; rr < 4; ++rr) {
-      inf[3 + 2 * rr] = 0;
-      inf[4 + 2 * rr] = 0;
-    }
-  }
+// seg_lo_r on, those at positions <= p - w'. One wave per query group finds the boundary with a
+// 64-ary search: each step probes 64 evenly spaced members at once. Returns (seg_lo, cnt) of
+// group r to every lane of the wave.
+__device__ __forceinline__ void seg_search(const int32_t* __restrict__ q_groups,
+                                           const int32_t* __restrict__ cache_off,
+                                           const int32_t* __restrict__ cache_idx, int b, int r,
+                                           int64_t p, int64_t wl, int64_t Lmax, int K, int top_k,
+                                           int l, int64_t* s0_out, int64_t* cnt_out) {
   const int g = q_groups[(int64_t)b * top_k + r];
   int64_t s0 = 0, cnt = 0;
   if (g >= 0 && g < K) {
@@ -79,28 +62,60 @@ __global__ __launch_bounds__(64) void decode_seg_kernel(const int32_t* __restric
     }
     cnt = lo_i - s0;
   }
-  if (l == 0) {
-    inf[3 + 2 * r] = (int32_t)s0;
-    inf[4 + 2 * r] = (int32_t)cnt;
-  }
+  *s0_out = s0;
+  *cnt_out = cnt;
 }
 
 // list[b][vi] = key position of virtual list entry vi, or -1 when the entry is a member of a
 // query group that a lower shared query group owns (so every allowed key is listed once).
+// Every block first builds its sequence's plan (waves 0 .. top_k - 1 search one query group
+// each); the sequence's first block also stores it in info[b] for the partial kernel.
 // With a page table the entry is the key's row in the shared page pool instead:
 // table[b][pos / page] * page + pos % page, or -1 when the table entry is not a page of the pool.
 __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restrict__ q_groups,
                                                           const int32_t* __restrict__ cache_groups,
+                                                          const int32_t* __restrict__ cache_len,
+                                                          const int32_t* __restrict__ cache_off,
                                                           const int32_t* __restrict__ cache_idx,
-                                                          const int32_t* __restrict__ info,
+                                                          int32_t* __restrict__ info,
                                                           int64_t Lmax, int K, int top_k,
-                                                          int64_t per_seq,
+                                                          int64_t window, int64_t per_seq,
                                                           const int32_t* __restrict__ table,
                                                           int page, int64_t pages_per_seq,
                                                           int64_t num_pages,
                                                           int32_t* __restrict__ list) {
   const int b = (int)(blockIdx.x / kListBlocks);
-  const int32_t* inf = info + (int64_t)b * kDecInfo;
+  __shared__ int32_t inf[kDecInfo];
+  {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    int64_t L = cache_len[b];
+    if (L < 1) L = 1;
+    if (L > Lmax) L = Lmax;
+    const int64_t p = L - 1;
+    const int64_t wl = window > 1 ? window : 1;  // the new token always sees itself
+    const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
+    if (w < top_k) {
+      int64_t s0, cnt;
+      seg_search(q_groups, cache_off, cache_idx, b, w, p, wl, Lmax, K, top_k, l, &s0, &cnt);
+      if (l == 0) {
+        inf[3 + 2 * w] = (int32_t)s0;
+        inf[4 + 2 * w] = (int32_t)cnt;
+      }
+    } else if (threadIdx.x == 64 * 3) {  // a lane of a wave without a search (top_k < 4)
+      for (int rr = top_k; rr < 4; ++rr) {
+        inf[3 + 2 * rr] = 0;
+        inf[4 + 2 * rr] = 0;
+      }
+    }
+    if (threadIdx.x == 0) {
+      inf[0] = (int32_t)lo;
+      inf[1] = (int32_t)(p - lo + 1);
+      inf[2] = 0;
+    }
+    __syncthreads();
+    if (blockIdx.x % kListBlocks == 0 && threadIdx.x < kDecInfo)
+      info[(int64_t)b * kDecInfo + threadIdx.x] = inf[threadIdx.x];
+  }
   const int64_t lo = inf[0], nl = inf[1];
   int64_t total = nl;
   for (int r = 0; r < top_k; ++r) total += inf[4 + 2 * r];
@@ -406,14 +421,10 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
                          int32_t* info, int32_t* list, float* part_o, float* part_ml,
                          uint16_t* out, float* lse, hipStream_t stream, const DecodePaging* pg) {
   const int64_t per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
-  hipLaunchKernelGGL(decode_seg_kernel, dim3((int64_t)s.B * s.top_k), dim3(64), 0, stream,
-                     q_groups, cache_len, cache_off, cache_idx, s.Lmax, s.K, s.top_k, s.window,
-                     info);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if (s.splits != kDecSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * kListBlocks), dim3(256),
-                     0, stream, q_groups, cache_groups, cache_idx, info, s.Lmax, s.K, s.top_k,
-                     per_seq, pg ? pg->table : nullptr, pg ? pg->page_size : 1,
+                     0, stream, q_groups, cache_groups, cache_len, cache_off, cache_idx, info,
+                     s.Lmax, s.K, s.top_k, s.window, per_seq, pg ? pg->table : nullptr, pg ? pg->page_size : 1,
                      pg ? pg->pages_per_seq : 0, pg ? pg->num_pages : 0, list);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   DecodeArgs a{};
