@@ -32,7 +32,8 @@ from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_siz
                                         focus_attention_workspace_size,
                                         focus_bucket, focus_bucket_append,
                                         focus_bucket_workspace_size, focus_decode,
-                                        focus_decode_paged,
+                                        focus_decode_paged, focus_decode_slots,
+                                        focus_slots_append, focus_slots_from_bucket,
                                         focus_soft_attention)
 from learned_centroid_gated_amd import _lib  # noqa: E402
 from synth import CONFIGS, assign_inputs, qkv_inputs, random_groups  # noqa: E402
@@ -445,6 +446,33 @@ def decode_bench(c, steps, warmup):
     res["paged16_kv_GBs"] = kv_bytes / (res["paged16_us_per_step"] * 1e-6) / 1e9
     log(f"[bench]   paged decode (16-token pages) {res['paged16_us_per_step']:.1f} us/step, "
         f"{res['paged16_kv_GBs']:.0f} GB/s")
+
+    # group-slotted memberships (a row of slots per sequence and group): decode over them, and
+    # the O(top_k) append of a new token's memberships
+    sizes = (off[:, 1:] - off[:, :-1]).max().item()
+    gcap = 1 << int(math.ceil(math.log2(sizes + 64)))
+    seg_len, seg_pos, overflow = focus_slots_from_bucket(off, idx, c.K, L, gcap)
+
+    def step_slots():
+        focus_decode_slots(qd, q_groups, kp, vp, table, lens, cache_groups, seg_len, seg_pos, c.K,
+                           c.window, out=out, lse=lse)
+
+    step_slots()
+    torch.cuda.synchronize()
+    assert int(overflow.item()) == 0, "slot rows overflowed"
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16)), "slotted decode differs"
+    for _ in range(warmup):
+        step_slots()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        step_slots()
+    e.record()
+    torch.cuda.synchronize()
+    res["slots_paged16_us_per_step"] = s.elapsed_time(e) * 1e3 / steps
+    res["slots_group_cap"] = gcap
+    log(f"[bench]   decode over slot rows (16-token pages) {res['slots_paged16_us_per_step']:.1f} "
+        f"us/step (group capacity {gcap})")
     del kp, vp, perm, table, out_ref
 
     # membership maintenance per step: the newest token of every cache joins the bucketed
@@ -476,6 +504,12 @@ def decode_bench(c, steps, warmup):
     del lens_prev, g_prev
     log(f"[bench]   append {res['append_us']:.1f} us/step ({res['append_GBs']:.0f} GB/s) vs "
         f"re-bucketing {res['rebucket_us']:.1f} us")
+    # the slotted append writes one position per membership (timed on rows that then hold the
+    # newest token again; they are not read afterwards)
+    res["slots_append_us"] = time_us(lambda: focus_slots_append(new_g, lens, seg_len, seg_pos,
+                                                                overflow, c.K))
+    log(f"[bench]   slot-row append {res['slots_append_us']:.1f} us/step")
+    del seg_len, seg_pos, overflow
     return res
 
 

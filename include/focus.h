@@ -299,6 +299,49 @@ int focus_decode_paged(const uint16_t* q, const int32_t* q_groups,
                        int64_t window, float scale, uint16_t* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Group-slotted cache memberships: an O(top_k) append per generated token (incremental
+ * decode, Chinese summary, section 2.1.3 inference: a new token joins its groups and attends
+ * their members). Each (sequence, group) owns a row of group_cap slots:
+ *
+ *   seg_len  device, [B, K] int32: members of group g of sequence b in use.
+ *   seg_pos  device, [B, K, group_cap] int32: their positions, ascending, in
+ *            seg_pos[b, g, 0 .. seg_len[b, g] - 1] (later slots unused).
+ *   overflow device, one int32 the calls set to 1 (never clear) when a group would need more
+ *            than group_cap slots; the members that do not fit are not stored, so the rows
+ *            must then be rebuilt with a larger capacity. The caller zeroes it.
+ *
+ * group_cap >= 1 and K * group_cap < 2^31. Asynchronous on `stream`.
+ *
+ * focus_slots_from_bucket fills the rows from focus_bucket output over cache_groups
+ * [B, Lmax, top_k] (offsets [B, K + 1], idx [B, Lmax * top_k]); batch <= 65535.
+ *
+ * focus_slots_append adds position cache_len[b] - 1 (the newest token of sequence b, larger
+ * than every stored position) to the rows of its groups new_groups[b, 0 .. top_k - 1], in
+ * place: one write per membership. Ids outside [0, K) are dropped and a repeated id joins
+ * once; sequences with cache_len[b] < 1 are left alone.
+ *
+ * focus_decode_slots is focus_decode_paged with the cache memberships read from the rows
+ * instead of a bucket; the results equal focus_decode_paged's on the same memberships.
+ *   group_cap <= Lmax is not required; cache_groups [B, Lmax, top_k] is still read for the
+ *   ownership rule. Other arguments, limits, workspace and errors as for focus_decode_paged.
+ * ------------------------------------------------------------------------------------ */
+int focus_slots_from_bucket(const int32_t* offsets, const int32_t* idx, int batch, int64_t Lmax,
+                            int K, int top_k, int group_cap, int32_t* seg_len, int32_t* seg_pos,
+                            int32_t* overflow, void* stream);
+int focus_slots_append(const int32_t* new_groups, const int32_t* cache_len, int batch, int K,
+                       int top_k, int group_cap, int32_t* seg_len, int32_t* seg_pos,
+                       int32_t* overflow, void* stream);
+int focus_decode_slots(const uint16_t* q, const int32_t* q_groups,
+                       const uint16_t* k_pages, const uint16_t* v_pages,
+                       int64_t num_pages, int page_size,
+                       const int32_t* page_table, int64_t pages_per_seq,
+                       const int32_t* cache_len, const int32_t* cache_groups,
+                       const int32_t* seg_len, const int32_t* seg_pos, int group_cap,
+                       int B, int Hq, int Hkv, int d_head, int K, int top_k,
+                       int64_t window, float scale, uint16_t* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

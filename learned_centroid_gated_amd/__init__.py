@@ -15,6 +15,9 @@ from .focus import (  # noqa: F401
     focus_bucket_workspace_size,
     focus_decode,
     focus_decode_paged,
+    focus_decode_slots,
+    focus_slots_append,
+    focus_slots_from_bucket,
     focus_decode_workspace_size,
     focus_soft_attention,
 )

@@ -31,6 +31,12 @@ SIGNATURES = {
     "focus_soft_attention": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_p, c_int, c_int,
                                      c_i64, c_f, c_f, c_p, c_p, c_p]),
     "focus_decode_workspace_size": (c_sz, [c_int, c_i64, c_int, c_int, c_int, c_int, c_int]),
+    "focus_slots_from_bucket": (c_int, [c_p, c_p, c_int, c_i64, c_int, c_int, c_int, c_p, c_p,
+                                        c_p, c_p]),
+    "focus_slots_append": (c_int, [c_p, c_p, c_int, c_int, c_int, c_int, c_p, c_p, c_p, c_p]),
+    "focus_decode_slots": (c_int, [c_p, c_p, c_p, c_p, c_i64, c_int, c_p, c_i64, c_p, c_p, c_p,
+                                   c_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_i64,
+                                   c_f, c_p, c_p, c_p, c_sz, c_p]),
     "focus_decode_paged": (c_int, [c_p, c_p, c_p, c_p, c_i64, c_int, c_p, c_i64, c_p, c_p, c_p,
                                    c_p, c_int, c_int, c_int, c_int, c_int, c_int, c_i64, c_f,
                                    c_p, c_p, c_p, c_sz, c_p]),

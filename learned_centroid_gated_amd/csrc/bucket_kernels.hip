@@ -228,4 +228,77 @@ hipError_t launch_bucket_append(const int32_t* new_groups, const int32_t* cache_
   return hipGetLastError();
 }
 
+// ============================================================================ group slots
+// Group-slotted memberships: the members of group g of sequence b are
+// seg_pos[(b * K + g) * gcap + i] for i < seg_len[b * K + g], positions ascending. A new token is
+// the newest of its sequence, so it joins each of its groups with one write at the end of that
+// group's row: O(top_k) work per token. overflow[0] is set to 1 (and never cleared here) when a
+// group would hold more than gcap members; those members are not stored.
+
+// Block (g, b) copies segment g of sequence b from a bucket (offsets and index lists of
+// capacity cap per sequence) into its row.
+__global__ __launch_bounds__(256) void slots_from_bucket_kernel(const int32_t* __restrict__ off,
+                                                                const int32_t* __restrict__ idx,
+                                                                int64_t cap, int K, int gcap,
+                                                                int32_t* __restrict__ seg_len,
+                                                                int32_t* __restrict__ seg_pos,
+                                                                int32_t* __restrict__ overflow) {
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int32_t* o = off + (int64_t)b * (K + 1);
+  int32_t s0 = o[g], s1 = o[g + 1];
+  if (s0 < 0 || s1 < s0 || (int64_t)s1 > cap) s0 = s1 = 0;  // not a bucket of this capacity
+  int32_t n = s1 - s0;
+  if (n > gcap) {
+    if (t == 0) overflow[0] = 1;
+    n = gcap;
+  }
+  const int32_t* src = idx + (int64_t)b * cap + s0;
+  int32_t* dst = seg_pos + ((int64_t)b * K + g) * gcap;
+  for (int32_t i = t; i < n; i += 256) dst[i] = src[i];
+  if (t == 0) seg_len[(int64_t)b * K + g] = n;
+}
+
+// Thread (b, r) appends position cache_len[b] - 1 to the row of the token's r-th group. Invalid
+// ids are dropped and a repeated id joins once, so no two threads touch one row.
+__global__ __launch_bounds__(64) void slots_append_kernel(const int32_t* __restrict__ new_groups,
+                                                          const int32_t* __restrict__ cache_len,
+                                                          int batch, int K, int top_k, int gcap,
+                                                          int32_t* __restrict__ seg_len,
+                                                          int32_t* __restrict__ seg_pos,
+                                                          int32_t* __restrict__ overflow) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= (int64_t)batch * top_k) return;
+  const int b = (int)(i / top_k), r = (int)(i % top_k);
+  const int32_t pos = cache_len[b] - 1;
+  const int g = new_groups[i];
+  if (pos < 0 || g < 0 || g >= K) return;
+  for (int r2 = 0; r2 < r; ++r2)
+    if (new_groups[(int64_t)b * top_k + r2] == g) return;
+  int32_t* len = seg_len + (int64_t)b * K + g;
+  const int32_t l = *len;
+  if (l < 0 || l >= gcap) {
+    overflow[0] = 1;
+    return;
+  }
+  seg_pos[((int64_t)b * K + g) * gcap + l] = pos;
+  *len = l + 1;
+}
+
+hipError_t launch_slots_from_bucket(const int32_t* off, const int32_t* idx, int batch, int64_t cap,
+                                    int K, int gcap, int32_t* seg_len, int32_t* seg_pos,
+                                    int32_t* overflow, hipStream_t stream) {
+  hipLaunchKernelGGL(slots_from_bucket_kernel, dim3(K, batch), dim3(256), 0, stream, off, idx,
+                     cap, K, gcap, seg_len, seg_pos, overflow);
+  return hipGetLastError();
+}
+
+hipError_t launch_slots_append(const int32_t* new_groups, const int32_t* cache_len, int batch,
+                               int K, int top_k, int gcap, int32_t* seg_len, int32_t* seg_pos,
+                               int32_t* overflow, hipStream_t stream) {
+  const int64_t n = (int64_t)batch * top_k;
+  hipLaunchKernelGGL(slots_append_kernel, dim3((n + 63) / 64), dim3(64), 0, stream, new_groups,
+                     cache_len, batch, K, top_k, gcap, seg_len, seg_pos, overflow);
+  return hipGetLastError();
+}
+
 }  // namespace focus

@@ -32,44 +32,35 @@ int decode_splits(const DecodeShape& s) {
 // ============================================================================ plan
 // info[b] = (lo, nl, 0, seg_lo_0, cnt_0, ..., seg_lo_3, cnt_3): the window is positions
 // lo .. lo + nl - 1; query group r contributes the cnt_r members of its segment from index
-// seg_lo_r on, those at positions <= p - w'. One wave per query group finds the boundary with a
-// 64-ary search: each step probes 64 evenly spaced members at once. Returns (seg_lo, cnt) of
-// group r to every lane of the wave.
-__device__ __forceinline__ void seg_search(const int32_t* __restrict__ q_groups,
-                                           const int32_t* __restrict__ cache_off,
-                                           const int32_t* __restrict__ cache_idx, int b, int r,
-                                           int64_t p, int64_t wl, int64_t Lmax, int K, int top_k,
-                                           int l, int64_t* s0_out, int64_t* cnt_out) {
-  const int g = q_groups[(int64_t)b * top_k + r];
-  int64_t s0 = 0, cnt = 0;
-  if (g >= 0 && g < K) {
-    const int32_t* off = cache_off + (int64_t)b * (K + 1);
-    const int32_t* cidx = cache_idx + (int64_t)b * Lmax * top_k;
-    s0 = off[g];
-    // first member index in [s0, s1) at a position > p - wl (positions ascend in a segment).
-    // Invariant: members below lo_i are at or before the boundary, members from hi_i on after.
-    // Lane l probes lo_i + span*l/64; the probes at or before the boundary form a prefix of
-    // n_le lanes, so the answer lies after the last of them and at or before the next.
-    const int64_t thr = p - wl;
-    int64_t lo_i = s0, hi_i = off[g + 1];
-    while (lo_i < hi_i) {
-      const int64_t span = hi_i - lo_i;
-      const bool le = (int64_t)cidx[lo_i + (span * l) / 64] <= thr;
-      const int n_le = __popcll(__ballot(le));
-      if (n_le == 0) break;  // even lo_i is past the boundary
-      if (n_le < 64) hi_i = lo_i + (span * n_le) / 64;
-      lo_i = lo_i + (span * (n_le - 1)) / 64 + 1;
-    }
-    cnt = lo_i - s0;
+// seg_lo_r on (indices into the sequence's member list), those at positions <= p - w'. One
+// wave per query group finds the boundary with a 64-ary search: each step probes 64 evenly
+// spaced members of [s0, s1) at once. Returns the count to every lane of the wave.
+__device__ __forceinline__ int64_t seg_search(const int32_t* __restrict__ members, int64_t s0,
+                                              int64_t s1, int64_t thr, int l) {
+  // first member index in [s0, s1) at a position > thr (positions ascend in a segment).
+  // Invariant: members below lo_i are at or before the boundary, members from hi_i on after.
+  // Lane l probes lo_i + span*l/64; the probes at or before the boundary form a prefix of
+  // n_le lanes, so the answer lies after the last of them and at or before the next.
+  int64_t lo_i = s0, hi_i = s1;
+  while (lo_i < hi_i) {
+    const int64_t span = hi_i - lo_i;
+    const bool le = (int64_t)members[lo_i + (span * l) / 64] <= thr;
+    const int n_le = __popcll(__ballot(le));
+    if (n_le == 0) break;  // even lo_i is past the boundary
+    if (n_le < 64) hi_i = lo_i + (span * n_le) / 64;
+    lo_i = lo_i + (span * (n_le - 1)) / 64 + 1;
   }
-  *s0_out = s0;
-  *cnt_out = cnt;
+  return lo_i - s0;
 }
 
 // list[b][vi] = key position of virtual list entry vi, or -1 when the entry is a member of a
 // query group that a lower shared query group owns (so every allowed key is listed once).
 // Every block first builds its sequence's plan (waves 0 .. top_k - 1 search one query group
 // each); the sequence's first block also stores it in info[b] for the partial kernel.
+// Memberships come bucketed (cache_off / cache_idx: offsets and one index list of capacity
+// Lmax * top_k per sequence) or, with seg_len, group-slotted (cache_idx holds seg_pos: a row of
+// gcap positions per (sequence, group), seg_len[b * K + g] of them in use). A listed position
+// outside [0, p] is skipped, and the list never exceeds its capacity per_seq.
 // With a page table the entry is the key's row in the shared page pool instead:
 // table[b][pos / page] * page + pos % page, or -1 when the table entry is not a page of the pool.
 __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restrict__ q_groups,
@@ -80,23 +71,41 @@ __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ info,
                                                           int64_t Lmax, int K, int top_k,
                                                           int64_t window, int64_t per_seq,
+                                                          const int32_t* __restrict__ seg_len,
+                                                          int gcap,
                                                           const int32_t* __restrict__ table,
                                                           int page, int64_t pages_per_seq,
                                                           int64_t num_pages,
                                                           int32_t* __restrict__ list) {
   const int b = (int)(blockIdx.x / kListBlocks);
   __shared__ int32_t inf[kDecInfo];
+  const int32_t* members = seg_len ? cache_idx + (int64_t)b * K * gcap
+                                   : cache_idx + (int64_t)b * Lmax * top_k;
+  int64_t L = cache_len[b];
+  if (L < 1) L = 1;
+  if (L > Lmax) L = Lmax;
+  const int64_t p = L - 1;
   {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    int64_t L = cache_len[b];
-    if (L < 1) L = 1;
-    if (L > Lmax) L = Lmax;
-    const int64_t p = L - 1;
     const int64_t wl = window > 1 ? window : 1;  // the new token always sees itself
     const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
     if (w < top_k) {
-      int64_t s0, cnt;
-      seg_search(q_groups, cache_off, cache_idx, b, w, p, wl, Lmax, K, top_k, l, &s0, &cnt);
+      const int g = q_groups[(int64_t)b * top_k + w];
+      int64_t s0 = 0, s1 = 0;
+      if (g >= 0 && g < K) {
+        if (seg_len) {
+          int64_t n = seg_len[(int64_t)b * K + g];
+          n = n < 0 ? 0 : (n > gcap ? gcap : n);
+          s0 = (int64_t)g * gcap;
+          s1 = s0 + n;
+        } else {
+          const int32_t* off = cache_off + (int64_t)b * (K + 1);
+          s0 = off[g];
+          s1 = off[g + 1];
+          if (s0 < 0 || s1 < s0 || s1 > per_seq) s0 = s1 = 0;  // not a bucket of this capacity
+        }
+      }
+      const int64_t cnt = seg_search(members, s0, s1, p - wl, l);
       if (l == 0) {
         inf[3 + 2 * w] = (int32_t)s0;
         inf[4 + 2 * w] = (int32_t)cnt;
@@ -111,6 +120,15 @@ __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restr
       inf[0] = (int32_t)lo;
       inf[1] = (int32_t)(p - lo + 1);
       inf[2] = 0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {  // the list holds at most per_seq entries
+      int64_t run = inf[1];
+      for (int r = 0; r < top_k; ++r) {
+        const int64_t room = per_seq - run;
+        if (inf[4 + 2 * r] > room) inf[4 + 2 * r] = (int32_t)room;
+        run += inf[4 + 2 * r];
+      }
     }
     __syncthreads();
     if (blockIdx.x % kListBlocks == 0 && threadIdx.x < kDecInfo)
@@ -131,7 +149,8 @@ __global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restr
       for (int r = 0; r < top_k; ++r) {
         const int64_t cnt = inf[4 + 2 * r];
         if (rem < cnt) {
-          const int cand = cache_idx[(int64_t)b * Lmax * top_k + inf[3 + 2 * r] + rem];
+          const int cand = members[inf[3 + 2 * r] + rem];
+          if (cand < 0 || cand > p) break;  // not a cached position: skipped
           // owned by g_r unless the key also holds a lower query group
           bool owned = true;
           const int32_t* kg = cache_groups + ((int64_t)b * Lmax + cand) * top_k;
@@ -419,12 +438,14 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
                          int32_t* info, int32_t* list, float* part_o, float* part_ml,
-                         uint16_t* out, float* lse, hipStream_t stream, const DecodePaging* pg) {
+                         uint16_t* out, float* lse, hipStream_t stream, const DecodePaging* pg,
+                         const DecodeSlots* sl) {
   const int64_t per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
   if (s.splits != kDecSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * kListBlocks), dim3(256),
                      0, stream, q_groups, cache_groups, cache_len, cache_off, cache_idx, info,
-                     s.Lmax, s.K, s.top_k, s.window, per_seq, pg ? pg->table : nullptr, pg ? pg->page_size : 1,
+                     s.Lmax, s.K, s.top_k, s.window, per_seq, sl ? sl->seg_len : nullptr,
+                     sl ? sl->gcap : 0, pg ? pg->table : nullptr, pg ? pg->page_size : 1,
                      pg ? pg->pages_per_seq : 0, pg ? pg->num_pages : 0, list);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   DecodeArgs a{};

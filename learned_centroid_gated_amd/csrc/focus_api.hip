@@ -154,7 +154,7 @@ const char* focus_status_string(int status) {
   }
 }
 
-int focus_version(void) { return 400; }  // 0.4.0: adds focus_decode_paged
+int focus_version(void) { return 500; }  // 0.5.0: adds the group-slotted membership entry points
 
 // ============================================================================ assign
 size_t focus_assign_workspace_size(int64_t n, int d, int d_g, int K) {
@@ -543,6 +543,87 @@ int focus_decode_paged(const uint16_t* q, const int32_t* q_groups, const uint16_
   return hip_status(launch_decode(q, q_groups, k_pages, v_pages, cache_len, cache_groups,
                                   cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
                                   w.part_ml, out, lse, (hipStream_t)stream, &pg));
+}
+
+int focus_slots_from_bucket(const int32_t* offsets, const int32_t* idx, int batch, int64_t Lmax,
+                            int K, int top_k, int group_cap, int32_t* seg_len, int32_t* seg_pos,
+                            int32_t* overflow, void* stream) {
+  if (batch < 1 || Lmax < 1 || group_cap < 1) return FOCUS_ERR_ARG;
+  if (int st = check_groups(K, top_k, 8)) return st;
+  if (Lmax * (int64_t)top_k >= kIdxLimit || (int64_t)batch > 65535 ||
+      (int64_t)K * group_cap >= kIdxLimit)
+    return FOCUS_ERR_SHAPE;
+  if (!offsets || !idx || !seg_len || !seg_pos || !overflow) return FOCUS_ERR_ARG;
+  if (!aligned4(offsets) || !aligned4(idx) || !aligned4(seg_len) || !aligned4(seg_pos) ||
+      !aligned4(overflow))
+    return FOCUS_ERR_ALIGN;
+  return hip_status(launch_slots_from_bucket(offsets, idx, batch, Lmax * top_k, K, group_cap,
+                                             seg_len, seg_pos, overflow, (hipStream_t)stream));
+}
+
+int focus_slots_append(const int32_t* new_groups, const int32_t* cache_len, int batch, int K,
+                       int top_k, int group_cap, int32_t* seg_len, int32_t* seg_pos,
+                       int32_t* overflow, void* stream) {
+  if (batch < 1 || group_cap < 1) return FOCUS_ERR_ARG;
+  if (int st = check_groups(K, top_k, 8)) return st;
+  if ((int64_t)K * group_cap >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  if (!new_groups || !cache_len || !seg_len || !seg_pos || !overflow) return FOCUS_ERR_ARG;
+  if (!aligned4(new_groups) || !aligned4(cache_len) || !aligned4(seg_len) || !aligned4(seg_pos) ||
+      !aligned4(overflow))
+    return FOCUS_ERR_ALIGN;
+  return hip_status(launch_slots_append(new_groups, cache_len, batch, K, top_k, group_cap, seg_len,
+                                        seg_pos, overflow, (hipStream_t)stream));
+}
+
+int focus_decode_slots(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_pages,
+                       const uint16_t* v_pages, int64_t num_pages, int page_size,
+                       const int32_t* page_table, int64_t pages_per_seq, const int32_t* cache_len,
+                       const int32_t* cache_groups, const int32_t* seg_len,
+                       const int32_t* seg_pos, int group_cap, int B, int Hq, int Hkv, int d_head,
+                       int K, int top_k, int64_t window, float scale, uint16_t* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || window < 0 || num_pages < 1 || page_size < 1 || pages_per_seq < 1 ||
+      group_cap < 1)
+    return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  if (num_pages > kIdxLimit / page_size || pages_per_seq > kIdxLimit / page_size)
+    return FOCUS_ERR_SHAPE;
+  const int64_t Lmax = pages_per_seq * page_size;
+  if (Lmax * (int64_t)top_k >= kIdxLimit || (int64_t)K * group_cap >= kIdxLimit)
+    return FOCUS_ERR_SHAPE;
+  if (B == 0) return FOCUS_OK;
+  if (!q || !q_groups || !k_pages || !v_pages || !page_table || !cache_len || !cache_groups ||
+      !seg_len || !seg_pos || !out || !lse)
+    return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned4(q_groups) || !aligned16(k_pages) || !aligned16(v_pages) ||
+      !aligned4(page_table) || !aligned4(cache_len) || !aligned4(cache_groups) ||
+      !aligned4(seg_len) || !aligned4(seg_pos) || !aligned16(out) || !aligned4(lse) ||
+      !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  const size_t need = focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+  DecodeShape s{};
+  s.B = B;
+  s.Lmax = Lmax;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
+  s.K = K;
+  s.top_k = top_k;
+  s.window = window;
+  s.scale = sc;
+  s.splits = decode_splits(s);
+  DecodeWs w;
+  decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  DecodePaging pg{page_table, page_size, pages_per_seq, num_pages};
+  DecodeSlots sl{seg_len, group_cap};
+  return hip_status(launch_decode(q, q_groups, k_pages, v_pages, cache_len, cache_groups, nullptr,
+                                  seg_pos, s, w.info, w.list, w.part_o, w.part_ml, out, lse,
+                                  (hipStream_t)stream, &pg, &sl));
 }
 
 }  // extern "C"

@@ -133,6 +133,14 @@ hipError_t launch_bucket_append(const int32_t* new_groups, const int32_t* cache_
                                 const int32_t* idx_in, int32_t* off_out, int32_t* idx_out,
                                 hipStream_t stream);
 
+// Group-slotted memberships (see bucket_kernels.hip): from a bucket, and the O(top_k) append.
+hipError_t launch_slots_from_bucket(const int32_t* off, const int32_t* idx, int batch, int64_t cap,
+                                    int K, int gcap, int32_t* seg_len, int32_t* seg_pos,
+                                    int32_t* overflow, hipStream_t stream);
+hipError_t launch_slots_append(const int32_t* new_groups, const int32_t* cache_len, int batch,
+                               int K, int top_k, int gcap, int32_t* seg_len, int32_t* seg_pos,
+                               int32_t* overflow, hipStream_t stream);
+
 // Attention pieces.
 struct AttnShape {
   int64_t n;     // tokens
@@ -194,12 +202,18 @@ struct DecodePaging {
   int page_size;
   int64_t pages_per_seq, num_pages;
 };
-// pg == nullptr: kc / vc are [B, Lmax, Hkv, dh] per-sequence caches.
+// Group-slotted cache memberships (cache_idx then holds seg_pos [B, K, gcap]; cache_off unused).
+struct DecodeSlots {
+  const int32_t* seg_len;  // [B, K]
+  int gcap;
+};
+// pg == nullptr: kc / vc are [B, Lmax, Hkv, dh] per-sequence caches. sl == nullptr: bucketed
+// cache memberships (cache_off [B, K + 1], cache_idx [B, Lmax * top_k]).
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
                          int32_t* info, int32_t* list, float* part_o, float* part_ml,
                          uint16_t* out, float* lse, hipStream_t stream,
-                         const DecodePaging* pg = nullptr);
+                         const DecodePaging* pg = nullptr, const DecodeSlots* sl = nullptr);
 
 }  // namespace focus

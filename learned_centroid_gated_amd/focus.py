@@ -256,3 +256,63 @@ def focus_decode_paged(q, q_groups, k_pages, v_pages, page_table, cache_len, cac
               int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
               ws.numel() * ws.element_size(), _stream(stream))
     return out, lse
+
+
+# ------------------------------------------------------------------ group-slotted memberships
+def focus_slots_from_bucket(offsets, idx, K, Lmax, group_cap, seg_len=None, seg_pos=None,
+                            overflow=None, stream=None):
+    """Rows of group_cap slots per (sequence, group) from a bucket (offsets [B, K+1], idx
+    [B, Lmax * top_k]): returns (seg_len [B, K], seg_pos [B, K, group_cap], overflow [1])."""
+    for t, name in ((offsets, "offsets"), (idx, "idx")):
+        _need(t, name, torch.int32)
+    dev = offsets.device
+    B = offsets.shape[0]
+    top_k = idx.shape[1] // Lmax
+    if seg_len is None:
+        seg_len = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if seg_pos is None:
+        seg_pos = torch.empty((B, K, group_cap), dtype=torch.int32, device=dev)
+    if overflow is None:
+        overflow = torch.zeros((1,), dtype=torch.int32, device=dev)
+    _lib_call("focus_slots_from_bucket", _ptr(offsets), _ptr(idx), B, int(Lmax), K, top_k,
+              int(group_cap), _ptr(seg_len), _ptr(seg_pos), _ptr(overflow), _stream(stream))
+    return seg_len, seg_pos, overflow
+
+
+def focus_slots_append(new_groups, cache_len, seg_len, seg_pos, overflow, K, stream=None):
+    """The newest token of every sequence joins the rows of its groups, in place."""
+    for t, name in ((new_groups, "new_groups"), (cache_len, "cache_len"), (seg_len, "seg_len"),
+                    (seg_pos, "seg_pos"), (overflow, "overflow")):
+        _need(t, name, torch.int32)
+    B, top_k = new_groups.shape
+    _lib_call("focus_slots_append", _ptr(new_groups), _ptr(cache_len), B, K, top_k,
+              seg_pos.shape[2], _ptr(seg_len), _ptr(seg_pos), _ptr(overflow), _stream(stream))
+
+
+def focus_decode_slots(q, q_groups, k_pages, v_pages, page_table, cache_len, cache_groups, seg_len,
+                       seg_pos, K, window, scale=0.0, out=None, lse=None, workspace=None,
+                       stream=None):
+    """focus_decode_paged with group-slotted cache memberships (seg_len [B, K], seg_pos
+    [B, K, group_cap]). Returns (out [B, Hq, dh] bf16, lse [B, Hq])."""
+    dev = q.device
+    for t, name in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, name, torch.bfloat16, dev)
+    for t, name in ((q_groups, "q_groups"), (page_table, "page_table"), (cache_len, "cache_len"),
+                    (cache_groups, "cache_groups"), (seg_len, "seg_len"), (seg_pos, "seg_pos")):
+        _need(t, name, torch.int32, dev)
+    B, Hq, dh = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    pages_per_seq = page_table.shape[1]
+    Lmax = pages_per_seq * page_size
+    top_k = q_groups.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_decode_workspace_size(B, Lmax, Hq, Hkv, dh, K, top_k), dev, workspace)
+    _lib_call("focus_decode_slots", _ptr(q), _ptr(q_groups), _ptr(k_pages), _ptr(v_pages),
+              num_pages, page_size, _ptr(page_table), pages_per_seq, _ptr(cache_len),
+              _ptr(cache_groups), _ptr(seg_len), _ptr(seg_pos), seg_pos.shape[2], B, Hq, Hkv, dh,
+              K, top_k, int(window), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(stream))
+    return out, lse

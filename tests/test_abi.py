@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -260,3 +260,48 @@ def test_decode_paged_validation(lib):
     assert _paged(lib, ws=None) == WS
     assert _paged(lib, wsb=16) == WS
     assert _paged(lib, B=0, q=None) == OK
+
+
+def test_slots_validation(lib):
+    fb = lambda off=P, idx=P, B=4, L=1024, K=16, k=2, cap=64, sl=P, sp=P, ov=P: \
+        lib.focus_slots_from_bucket(off, idx, B, L, K, k, cap, sl, sp, ov, None)
+    assert fb(B=0) == ARG
+    assert fb(L=0) == ARG
+    assert fb(cap=0) == ARG
+    assert fb(K=0) == ARG
+    assert fb(k=9) == UNSUP
+    assert fb(B=70000) == SHAPE
+    assert fb(K=1024, cap=1 << 21) == SHAPE
+    for name in ("off", "idx", "sl", "sp", "ov"):
+        assert fb(**{name: None}) == ARG, name
+    assert fb(sp=P + 2) == ALIGN
+    ap = lambda ng=P, ln=P, B=4, K=16, k=2, cap=64, sl=P, sp=P, ov=P: \
+        lib.focus_slots_append(ng, ln, B, K, k, cap, sl, sp, ov, None)
+    assert ap(B=0) == ARG
+    assert ap(cap=0) == ARG
+    assert ap(K=1024, cap=1 << 21) == SHAPE
+    for name in ("ng", "ln", "sl", "sp", "ov"):
+        assert ap(**{name: None}) == ARG, name
+    assert ap(ov=P + 1) == ALIGN
+
+
+def _dslots(lib, q=P, qg=P, kp=P, vp=P, npages=64, page=16, table=P, pps=8, ln=P, cg=P, sl=P,
+            sp=P, cap=64, B=4, Hq=8, Hkv=2, dh=128, K=16, top_k=2, window=64, scale=0.0, out=P,
+            lse=P, ws=P, wsb=BIG):
+    return lib.focus_decode_slots(q, qg, kp, vp, npages, page, table, pps, ln, cg, sl, sp, cap, B,
+                                  Hq, Hkv, dh, K, top_k, window, scale, out, lse, ws, wsb, None)
+
+
+def test_decode_slots_validation(lib):
+    assert _dslots(lib, B=-1) == ARG
+    assert _dslots(lib, cap=0) == ARG
+    assert _dslots(lib, page=0) == ARG
+    assert _dslots(lib, dh=32) == UNSUP
+    assert _dslots(lib, K=1024, cap=1 << 21) == SHAPE
+    assert _dslots(lib, npages=(1 << 27) + 1, page=16) == SHAPE
+    for name in ("q", "qg", "kp", "vp", "table", "ln", "cg", "sl", "sp", "out", "lse"):
+        assert _dslots(lib, **{name: None}) == ARG, name
+    assert _dslots(lib, sp=P + 2) == ALIGN
+    assert _dslots(lib, ws=None) == WS
+    assert _dslots(lib, wsb=16) == WS
+    assert _dslots(lib, B=0, q=None) == OK
