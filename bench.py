@@ -548,7 +548,7 @@ def cpu_baseline(c, budget_s=20.0):
     tok_s = 1.0 / (t_assign + t_attn)
     return {"value": tok_s, "unit": "tokens/s", "cores": cores, "blas_threads": threads,
             "kind": "oracle",
-            "sample": f"assign_ref on {n_a} tokens of the {c.name} shapes ({t_assign * n_a:.1f}s) "
+            "sample": f"assign_ref on {n_a} tokens of the {c.name} shapes ({t_assign * n_a:.3f}s) "
                       f"+ attention_rows_ref on {len(rows)} uniformly drawn rows of the full "
                       f"{c.n}-token sequence ({t_rows:.1f}s); tokens/s = 1/(s/token + s/row)"}
 
