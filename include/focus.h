@@ -11,7 +11,8 @@
  *   (ZH)  "Why Attend to Everything? Focus is the Key", Chinese technical summary
  *         (gist.science/zh), sections 2.1.1 token grouping, 2.1.2 gated attention,
  *         2.1.3 top-k inference.
- *   (NL)  Same title, Dutch technical summary (gist.science/nl), "Kerncomponenten" 1-4.
+ *   (NL)  Same title, Dutch technical summary (gist.science/nl), "Kerncomponenten" 1-4,
+ *         "Resultaten".
  *   (ABS) Same title, English abstract (arxivdaily.com).
  *
  * Conventions shared by every entry point
@@ -24,8 +25,9 @@
  *     FOCUS_ERR_ALIGN). Tensors are dense and row-major in the shapes given. bf16 tensors are
  *     passed as uint16_t bit patterns.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
- *     returns without waiting. Inputs are never written. Calls are re-entrant; two calls
- *     that share a workspace must not overlap in time.
+ *     returns without waiting. Inputs are never written (focus_slots_append updates the
+ *     membership rows it is given in place). Calls are re-entrant; two calls that share a
+ *     workspace, or rows being appended to, must not overlap in time.
  *   - Arguments are validated on the host before anything is enqueued; an invalid call
  *     returns a negative status and enqueues nothing. A failed launch returns FOCUS_ERR_HIP.
  *     No C++ exception crosses this interface.
