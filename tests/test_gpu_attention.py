@@ -40,6 +40,8 @@ CASES = [
     (2000, 64, 8, 128, 128, 2, 1024, 1.1),
     (3000, 32, 8, 128, 256, 1, 512, 0),
     (1500, 8, 8, 64, 5, 4, 33, 0.7),
+    (3000, 16, 1, 64, 1024, 4, 100, 0),   # largest K and top_k, G = 16
+    (2500, 16, 1, 128, 1024, 3, 0, 0),
 ]
 
 

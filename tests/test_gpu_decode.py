@@ -26,6 +26,7 @@ def run_decode(qd, q_groups, kc, vc, lens, cache_groups, K, window):
     (6, 257, 2, 1, 64, 3, 2, 400),
     (2, 700, 64, 8, 128, 16, 2, 32),
     (3, 900, 32, 2, 64, 16, 1, 64),
+    (2, 3000, 16, 1, 64, 1024, 4, 100),  # largest K and top_k, G = 16
 ])
 def test_decode_matches_oracle(B, L, Hq, Hkv, dh, K, k, w):
     say(f"decode B={B} L={L} Hq={Hq} Hkv={Hkv} dh={dh} K={K} top_k={k} window={w}")
