@@ -63,3 +63,21 @@ def test_soft_large_lambda_reaches_hard_rule(Hq, Hkv):
     dl = np.abs(to_np(lse_s) - to_np(lse_h))
     say(f"  soft(lambda=200) vs hard: max|dO|={d.max():.2e} max|dLSE|={dl.max():.2e}")
     assert d.max() <= 2e-2 and dl.max() <= 2e-3
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (4, 2)])
+def test_soft_custom_scale(Hq, Hkv):
+    """A caller-given logit scale: the bias-row path (G >= 8) divides the biases by it and adds
+    the row shift back in natural units; the per-element path (G < 8) adds the biases directly.
+    Scale 0.3 at head size 64 (logit spread about 2.4), as in the attention tests: at head size
+    128 the softmax is so peaked that bf16 weights and outputs alone approach the 2e-2 bound."""
+    from learned_centroid_gated_amd import focus_soft_attention
+    n, dh, K, k, w, lam, scale = 800, 64, 9, 2, 50, 7.0, 0.3
+    say(f"soft custom scale Hq={Hq} Hkv={Hkv} scale={scale}")
+    t = qkv_inputs(n, Hq, Hkv, dh, index=0, salt=611)
+    groups = random_groups(n, K, k, np.random.default_rng(611))
+    out, lse = focus_soft_attention(bf16_dev(t["q"]), bf16_dev(t["k"]), bf16_dev(t["v"]),
+                                    i32_dev(groups), K, w, lam, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = soft_gate_ref(t["q"], t["k"], t["v"], groups, w, lam, scale=scale, with_lse=True)
+    check_attention(out, lse, o_ref, l_ref, "soft, scale 0.3")
