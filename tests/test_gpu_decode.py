@@ -90,3 +90,20 @@ def test_decode_workload_oracle_memberships():
                           i32_dev(cache_groups), c.K, c.window)
     o_ref, l_ref = decode_ref(qd, qg, t["k"], t["v"], lens, cache_groups, c.window)
     check_attention(out, lse, o_ref, l_ref, "decode workload")
+
+
+def test_decode_custom_scale():
+    from learned_centroid_gated_amd import focus_bucket, focus_decode
+    B, L, Hq, Hkv, dh, K, k, w, scale = 3, 900, 8, 2, 64, 8, 2, 40, 0.3
+    rng = np.random.default_rng(31)
+    t = qkv_inputs(L, Hq, Hkv, dh, index=0, salt=431, lead=(B,))
+    cache_groups = np.stack([random_groups(L, K, k, rng) for _ in range(B)])
+    q_groups = np.stack([random_groups(1, K, k, rng)[0] for _ in range(B)])
+    lens = np.array([L, 5, L // 2], np.int32)
+    qd = np.stack([t["q"][b, lens[b] - 1] for b in range(B)])
+    off, idx, _ = focus_bucket(i32_dev(cache_groups), K)
+    out, lse = focus_decode(bf16_dev(qd), i32_dev(q_groups), bf16_dev(t["k"]), bf16_dev(t["v"]),
+                            i32_dev(lens), i32_dev(cache_groups), off, idx, K, w, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = decode_ref(qd, q_groups, t["k"], t["v"], lens, cache_groups, w, scale=scale)
+    check_attention(out, lse, o_ref, l_ref, "decode, scale 0.3")
