@@ -320,11 +320,11 @@ def _soft_gate_logits(q, k, groups, window, lam, scale, literal):
     g = np.asarray(groups)
     share = (g[:, None, :, None] == g[None, :, None, :]).any(axis=(2, 3))
     a = share.astype(np.float64) - 0.5                         # group affinity
-    gate = 1.0 / (1.0 + np.exp(-lam * a))
+    log_gate = -np.logaddexp(0.0, -lam * a)                    # log sigmoid(lambda * a)
     if literal:
-        s = s * np.where(local, 1.0, gate)[None]
+        s = s * np.where(local, 1.0, np.exp(log_gate))[None]
     else:
-        s = s + np.where(local, 0.0, np.log(gate))[None]
+        s = s + np.where(local, 0.0, log_gate)[None]
     return np.where((j <= i)[None], s, -np.inf)
 
 

@@ -140,3 +140,17 @@ def test_balanced_groups_are_roughly_equal():
     r = assign_ref(a["hidden"], a["w_g"], a["centroids"], 1, 3)
     sizes = np.bincount(r["groups"][:, 0], minlength=16)
     assert sizes.min() > 0.5 * 4096 / 16 and sizes.max() < 1.6 * 4096 / 16
+
+
+def test_balanced_ranking_golden():
+    """Hand-worked case in which one Sinkhorn iteration moves token 2's top-1 away from its raw
+    argmax: ranking by raw scores, by S - v, or by the row-only plan all fail it."""
+    g = load_golden("balanced_rank_n3.json")
+    h, w, c = (np.array(g[x], np.float64) for x in ("hidden", "w_g", "centroids"))
+    ref = assign_ref(h, w, c, 1, g["iters"])
+    np.testing.assert_allclose(ref["v"], np.array(g["v"]), rtol=0, atol=1e-12)
+    plan = np.exp(ref["S"] + ref["u"][:, None] + ref["v"][None, :])
+    np.testing.assert_allclose(plan, np.array(g["plan"]), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(ref["groups"], np.array(g["top1_groups"]))
+    raw = assign_ref(h, w, c, 1, 0)
+    np.testing.assert_array_equal(raw["groups"], np.array(g["top1_groups_raw"]))
