@@ -228,31 +228,6 @@ def test_decode_validation(lib):
     assert _decode(lib, B=0, q=None) == OK
 
 
-def test_python_binding_refuses_host_tensors():
-    import torch
-    import learned_centroid_gated_amd as F
-    with pytest.raises(ValueError, match="device tensor"):
-        F.focus_assign(torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(2, 4), 1, 1)
-    bf = torch.zeros(8, 2, 64, dtype=torch.bfloat16)
-    i1 = torch.zeros(9, dtype=torch.int32)
-    i2 = torch.zeros(8, 2, dtype=torch.int32)
-    calls = [
-        lambda: F.focus_bucket(i2, 4),
-        lambda: F.focus_attention(bf, bf, bf, i2, i1, i1, i2, 4, 2),
-        lambda: F.focus_attention_asym(bf, bf, bf, (i1, i1, i2), (i1, i1, i2[:, :1]), 4, 2),
-        lambda: F.focus_soft_attention(bf, bf, bf, i2, 4, 2, 1.0),
-        lambda: F.focus_bucket_append(i2, i1, i2, i2, 4, 8),
-        lambda: F.focus_decode_paged(bf, i2, bf[None], bf[None], i2, i1, i2[None], i2, i2, 4, 2),
-        lambda: F.focus_slots_from_bucket(i2, i2, 4, 8, 16),
-        lambda: F.focus_slots_append(i2, i1, i2, i2[None], i1, 4),
-        lambda: F.focus_decode_slots(bf, i2, bf[None], bf[None], i2, i1, i2[None], i2, i2[None],
-                                     4, 2),
-    ]
-    for call in calls:  # refused on the host, before any library call
-        with pytest.raises(ValueError, match="device tensor"):
-            call()
-
-
 @pytest.mark.gpu
 def test_python_binding_checks_dtypes():
     import torch
