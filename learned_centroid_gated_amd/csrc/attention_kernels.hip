@@ -245,7 +245,9 @@ struct FlashArgs {
   const int32_t* groups;    // soft gate: [n, top_k] memberships
   float soft_b0, soft_b1;   // soft gate: far-pair logit bias without / with a shared group,
                             // in raw q.k units (log sigmoid(lambda * (share - 1/2)) / scale)
-  float soft_shift;         // soft gate with bias rows: soft_b0 in natural-log units
+  float soft_shift;         // soft gate with bias rows: the row shift, max(b0, b1), natural log
+  int soft_mark_none;       // soft gate with bias rows: the rows mark pairs sharing no group
+                            // (b1 > b0, lambda > 0), else pairs sharing one
 };
 
 constexpr int KT = 64;  // keys per kv tile
@@ -415,13 +417,16 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
   // query side of the ownership bias: -2^100 at this row's token (T <= 32: token = jq % T)
   bf16x8_t qm[MKS > 0 ? MKS : 1];
-  // soft gate with bias rows: logits are shifted by -soft_b0 for every pair of a row (lse adds
-  // it back), so far pairs need only c = soft_b1 - soft_b0 times share. The MFMA adds it as the
-  // three bf16 parts of c (8 + 8 + 8 significand bits hold all of fp32, so the sum is c
-  // exactly), one k-step each over the same share rows
-  float soft_c = 0.f;
+  // soft gate with bias rows: every logit of a row is shifted by minus the larger far-pair bias
+  // (lse adds it back), so the far pairs that carry the smaller bias need c = smaller - larger
+  // (<= 0) and the others nothing: the large offsets land on suppressed pairs and the dominant
+  // logits stay exact at any lambda. The rows mark the pairs that carry c; the MFMA adds c as
+  // its three bf16 parts (8 + 8 + 8 significand bits hold all of fp32, so the sum is c
+  // exactly), one k-step each over the same marked rows
+  float soft_c = 0.f, soft_sh = 0.f;
   if constexpr (SBIAS) {
-    const float c = a.soft_b1 - a.soft_b0;
+    soft_sh = a.soft_mark_none ? a.soft_b1 : a.soft_b0;
+    const float c = a.soft_mark_none ? a.soft_b0 - a.soft_b1 : a.soft_b1 - a.soft_b0;
     const __bf16 c0 = to_bf16(c);
     const __bf16 c1 = to_bf16(c - (float)c0);
     const __bf16 c2 = to_bf16(c - (float)c0 - (float)c1);
@@ -606,8 +611,10 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       m |= (uint32_t)dpp_move_i<0x4E>((int)m);
       if (tq == 0) sb.kpos[kkey] = (int)m;
       if constexpr (SBIAS) {
-        // share rows (T <= 16): thread tq writes tokens [4 tq, 4 tq + 4) of the key's row;
+        // marked rows (T <= 16): thread tq writes tokens [4 tq, 4 tq + 4) of the key's row, 1.0
+        // where the pair carries c (shares a group, or shares none when soft_mark_none);
         // entries of tokens past T are never selected by a row's one-hot
+        const bool mark_none = a.soft_mark_none != 0;
         uint32_t w2[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
           uint32_t tm = 0;  // slots of token t
 #pragma unroll
           for (int c = 0; c < TK; ++c) tm |= (t < a.T && c * a.T + t < 32) ? 1u << (c * a.T + t) : 0u;
-          w2[e >> 1] |= (m & tm) ? (0x3F80u << (16 * (e & 1))) : 0u;
+          w2[e >> 1] |= (((m & tm) != 0u) != mark_none) ? (0x3F80u << (16 * (e & 1))) : 0u;
         }
         const i32x2_t wv = {(int)w2[0], (int)w2[1]};
         *(i32x2_t*)&sb.mrow[0][kkey][4 * tq] = wv;
@@ -661,13 +668,17 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
 
     // ------------------------------------------------------------ S^T = K Q^T (+ bias)
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-    if constexpr (SBIAS) {  // one share row block, one k-step per part of c
+    if constexpr (SBIAS) {
+      // one marked row block, one k-step per part of c; only in tiles whose pairs are all far
+      // (edge tiles add the term per element, so near pairs never carry it)
+      if (cls == kFull) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t mf = *(const bf16x8_t*)(lds + mrd + par + kb * 32 * 32);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8_t mf = *(const bf16x8_t*)(lds + mrd + par + kb * 32 * 32);
 #pragma unroll
-        for (int j = 0; j < MKS; ++j)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, qm[j], sacc[kb], 0, 0, 0);
+          for (int j = 0; j < MKS; ++j)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, qm[j], sacc[kb], 0, 0, 0);
+        }
       }
     } else if constexpr (MKS > 0) {
 #pragma unroll
@@ -702,7 +713,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
       // keep 2 * KPF operand reads in flight: the scheduler would otherwise sink each read
       // next to its MFMA (masks: 0x100 LDS read, 0x008 MFMA); the bias step's operands, when
       // present, are read first like the K fragments
-      constexpr int NM = 2 * (NS + MKS);  // MFMAs of the S product, each with one LDS read
+      constexpr int NM = 2 * (NS + (SBIAS ? 0 : MKS));  // MFMAs of the S product, one LDS read each
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
 #pragma unroll
       for (int i = 0; i < NM - 2 * KPF; ++i) {
@@ -760,8 +771,9 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(const FlashArgs a) {
             for (int e = 0; e < 4; ++e) {
               const int dd = qi - (ks + kk0 + e);
               ok[e] = dd >= 0;
-              if constexpr (SBIAS) {  // near pairs: undo the share term, take the row shift
-                if (dd < window) sacc[kb][4 * q4 + e] -= a.soft_b0 + (share[e] ? soft_c : 0.f);
+              if constexpr (SBIAS) {  // near pairs take the row shift, far pairs the marked term
+                const bool marked = share[e] != (a.soft_mark_none != 0);
+                sacc[kb][4 * q4 + e] += dd < window ? -soft_sh : (marked ? soft_c : 0.f);
               } else {
                 if (dd >= window) sacc[kb][4 * q4 + e] += share[e] ? a.soft_b1 : a.soft_b0;
               }
@@ -1160,7 +1172,9 @@ hipError_t launch_soft_attention(const uint16_t* q, const uint16_t* k, const uin
   fa.sl2 = s.scale * kLog2e;
   fa.soft_b0 = bias_none / s.scale;
   fa.soft_b1 = bias_share / s.scale;
-  fa.soft_shift = bias_none;
+  // bias-row path: rows shift by the larger bias, the rows mark the pairs with the smaller one
+  fa.soft_mark_none = bias_share > bias_none ? 1 : 0;
+  fa.soft_shift = bias_share > bias_none ? bias_share : bias_none;
   fa.tiles_per_head = (int)((s.n + fa.T - 1) / fa.T);
   const int64_t blocks = xcd_grid((int64_t)s.Hkv * fa.tiles_per_head);
   if (blocks <= 0) return hipSuccess;

@@ -83,13 +83,14 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 // whole copy before the first LDS read that follows, which serialises the prefetch of the next
 // tile with the compute on the current one. The caller waits (vmcnt) before the data is read.
 // The LDS destination goes in as a pointer operand (not an integer), so the compiler keeps
-// treating the buffer as written by the asm statement.
+// treating the buffer as written by the asm statement; m0 is listed as clobbered, since the
+// statement overwrites it with that destination.
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, void* lds_dst) {
   lds_char_t* m = (lds_char_t*)lds_dst;
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(base), "s"(m)
-               : "memory");
+               : "memory", "m0");
 }
 
 // s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt at their maxima)

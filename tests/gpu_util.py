@@ -7,7 +7,8 @@ import torch
 
 TOL_MAX_ABS = 2e-2   # attention output, bf16 inputs against the fp64 oracle
 TOL_MEAN_ABS = 2e-3
-TOL_LSE = 2e-3       # the log-sum-exp is accumulated in fp32 from exact bf16 products
+TOL_LSE = 1e-4       # the log-sum-exp is accumulated in fp32 from exact bf16 products; one
+                     # double-counted or missing pair in a row of m keys moves it by about 1/m
 
 
 def say(*msg):

@@ -32,6 +32,11 @@ CASES = [
     (1300, 8, 1, 64, 5, 1, 37, -8.0),
     (640, 16, 2, 128, 6, 2, 64, 60.0),
     (520, 16, 2, 128, 6, 2, 40, 1000.0),  # the share term's parts must add up to it exactly
+    # |lambda| large: each row shifts by the larger bias, so kept logits carry no large offset
+    (520, 16, 2, 128, 6, 2, 40, 1e5),
+    (530, 16, 2, 128, 6, 2, 40, -1e5),
+    (600, 8, 2, 64, 5, 2, 32, 1e5),
+    (1100, 32, 2, 128, 9, 1, 0, 3e4),
 ]
 
 
