@@ -86,3 +86,42 @@ def test_assign_full_size(name):
     # Sinkhorn's balance shows in the hard group sizes
     sizes = np.bincount(g.ravel(), minlength=c.K)
     say(f"  group sizes min={sizes.min()} mean={sizes.mean():.1f} max={sizes.max()}")
+
+
+def _assign_device_inputs(c, n=None):
+    """The workload's inputs drawn on the device (the bench's generator), plus host copies."""
+    n = c.n if n is None else n
+    a = assign_inputs(n, c.d, c.dg, c.K, c.mix, c.weights, c.noise_frac, index=c.index,
+                      device="cuda")
+    return a, {x: a[x].cpu().numpy() for x in ("hidden", "w_g", "centroids")}
+
+
+def _compare_device_run(c, a, host):
+    from learned_centroid_gated_amd import focus_assign
+    groups, v = focus_assign(a["hidden"], a["w_g"], a["centroids"], c.top_k, c.iters)
+    torch.cuda.synchronize()
+    g, v = to_np(groups), to_np(v)
+    say("  GPU done; oracle ...")
+    ref = assign_ref(host["hidden"], host["w_g"], host["centroids"], c.top_k, c.iters)
+    np.testing.assert_allclose(v, ref["v"], rtol=0, atol=2e-5)
+    _check_groups(g, ref, ref["S"] + ref["v"][None, :])
+    sizes = np.bincount(g.ravel(), minlength=c.K)
+    say(f"  group sizes min={sizes.min()} mean={sizes.mean():.1f} max={sizes.max()}")
+
+
+def test_assign_long_context_shapes_at_64k_tokens():
+    """The 1M-token workload's shapes (d 4096, d_g 128, K 256, top-1, two iterations, 10% noise
+    tokens) at n = 65536: the same two-product plan and kernels as the full size."""
+    c = [x for x in CONFIGS if x.name == "long_n1m"][0]
+    say(f"assign long_n1m shapes at n=65536: d={c.d} dg={c.dg} K={c.K}")
+    a, host = _assign_device_inputs(c, 65536)
+    _compare_device_run(c, a, host)
+
+
+@pytest.mark.timeout(900)
+def test_assign_full_size_long_n1m():
+    """The 1M-token workload at full size, inputs drawn exactly as the benchmark draws them."""
+    c = [x for x in CONFIGS if x.name == "long_n1m"][0]
+    say(f"assign full size long_n1m: n={c.n} d={c.d} (17 GB of hidden states; oracle ~1-2 min)")
+    a, host = _assign_device_inputs(c)
+    _compare_device_run(c, a, host)
