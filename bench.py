@@ -140,7 +140,16 @@ def count_allowed_pairs(q, k, v, groups, off, idx, slot, K, window):
     return int(counts.sum().item())
 
 
-def prefill_bench(c, steps, warmup, hip):
+def sample_rows(n, window, rng):
+    """Stratified query rows for the oracle check: the first rows (inside the first window),
+    the last rows, and rows drawn uniformly in between."""
+    first = np.arange(min(n, 32))
+    last = np.arange(max(0, n - 32), n)
+    mid = rng.integers(0, n, size=min(n, 64))
+    return np.unique(np.concatenate([first, last, mid]))
+
+
+def prefill_bench(c, steps, warmup, hip, capture=False):
     log(f"[bench] prefill {c.name}: n={c.n} d={c.d} Hq={c.Hq}/{c.Hkv} dh={c.dh} K={c.K} "
         f"top_k={c.top_k} window={c.window} iters={c.iters}")
     t0 = time.time()
@@ -197,6 +206,17 @@ def prefill_bench(c, steps, warmup, hip):
     wall = time.time() - wall0
     total_ms = start.elapsed_time(end)
     ms = total_ms / steps
+    cap = None
+    if capture:
+        # what the oracle leg needs to check this very step: its inputs, its memberships and
+        # column potential, and the timed step's output on stratified sample rows
+        rows = sample_rows(c.n, c.window, np.random.default_rng(c.index + 11))
+        rows_t = torch.from_numpy(rows).to(dev)
+        bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+        cap = {"hidden": hidden.cpu().numpy(), "w_g": w_g.cpu().numpy(),
+               "centroids": cents.cpu().numpy(), "v": vpot.cpu().numpy(),
+               "q": bits(q), "k": bits(k), "v_in": bits(v), "rows": rows,
+               "out_rows": out[rows_t].float().cpu().numpy(), "lse_rows": lse[rows_t].cpu().numpy()}
     assign_ms = np.mean([hip.elapsed_ms(e[0], e[1]) for e in call_ev])
     bucket_ms = np.mean([hip.elapsed_ms(e[1], e[2]) for e in call_ev])
     stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * s], e[2 * s + 1]) for e in stage_ev]))
@@ -220,7 +240,13 @@ def prefill_bench(c, steps, warmup, hip):
         "allowed_pairs": pairs, "window_pairs": wpairs, "group_pairs": gpairs,
         "density_vs_causal": pairs / (c.n * (c.n + 1) / 2),
         "segment_sizes": {"min": int(sizes.min()), "mean": float(sizes.mean()), "max": int(sizes.max())},
+        "pairs_source": "Q = 0 run of the product path (exp(lse) counts each row's keys)",
     }
+    # the memberships, kept on the host for the oracle leg's recount of the allowed pairs
+    res["_groups"] = groups.cpu().numpy()
+    if cap is not None:
+        cap["groups"] = res["_groups"]
+        res["_capture"] = cap
     attn_ms = stage_ms["group_attention"] + stage_ms["window_attention_merge"]
     res["attention_tflops"] = flops_pair * pairs / (attn_ms * 1e-3) / 1e12
     res["attention_pct_bf16_peak"] = 100 * res["attention_tflops"] / PEAK_BF16_TFLOPS
@@ -514,43 +540,65 @@ def decode_bench(c, steps, warmup):
 
 
 # ------------------------------------------------------------------ oracle on the host
-def cpu_baseline(c, budget_s=20.0):
-    """The oracle, untuned, on a bounded sample of the same workload: assignment of a block of
-    tokens with the workload's shapes, plus attention rows drawn uniformly from the full
-    sequence; tokens/s = 1 / (assign seconds per token + attention seconds per row)."""
-    from oracle import assign_ref, attention_rows_ref
+def cpu_baseline(c, cap, prefill):
+    """The oracle leg, on the host cores of the same run. It times the untuned oracle on a bounded
+    sample of the headline workload and checks the timed step against it:
+      - assign_ref over the step's full hidden states (groups bit-exact outside the tie window,
+        column potential), timed per token;
+      - attention_rows_ref on stratified rows of the full sequence with the step's memberships,
+        timed per row and compared with the step's output on those rows;
+      - pair_count_ref over every benchmarked workload's memberships, which must equal the
+        allowed-pair count behind its effective FLOPs.
+    tokens/s = 1 / (assign seconds per token + attention seconds per row)."""
+    from oracle import TIE_LOG, assign_ref, attention_rows_ref, pair_count_ref
     try:
         from threadpoolctl import threadpool_info
         threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
     except Exception:
         threads = None
     cores = len(os.sched_getaffinity(0))
-    n_a = min(c.n, 4096)
-    a = assign_inputs(n_a, c.d, c.dg, c.K, c.mix, c.weights, c.noise_frac, index=c.index, salt=7)
     t0 = time.time()
-    assign_ref(a["hidden"], a["w_g"], a["centroids"], c.top_k, c.iters)
-    t_assign = (time.time() - t0) / n_a
-    del a
-    kv = qkv_inputs(c.n, c.Hq, c.Hkv, c.dh, index=c.index, salt=8, which="kv")
-    groups = random_groups(c.n, c.K, c.top_k, np.random.default_rng(c.index))
-    rng = np.random.default_rng(1)
-    rows, t_rows = [], 0.0
-    while t_rows < budget_s and len(rows) < 256:
-        i = int(rng.integers(c.n))
-        # the oracle reads q only at row i: a stride-0 view stands in for the full array
-        q_row = qkv_inputs(1, c.Hq, 1, c.dh, index=c.index, salt=10 + len(rows), which="q")["q"]
-        qi = np.broadcast_to(q_row, (c.n, c.Hq, c.dh))
-        t0 = time.time()
-        attention_rows_ref(qi, kv["k"], kv["v"], groups, c.window, rows=[i])
-        t_rows += time.time() - t0
-        rows.append(i)
-    t_attn = t_rows / len(rows)
-    tok_s = 1.0 / (t_assign + t_attn)
+    ref = assign_ref(cap["hidden"], cap["w_g"], cap["centroids"], c.top_k, c.iters)
+    t_assign = time.time() - t0
+    same = (ref["groups"] == cap["groups"]).all(axis=1)
+    unflagged = int((~same & ~ref["tie"]).sum())
+    v_err = float(np.abs(ref["v"] - cap["v"]).max())
+    del cap["hidden"]
+    rows = cap["rows"]
+    t0 = time.time()
+    o_ref, l_ref = attention_rows_ref(cap["q"], cap["k"], cap["v_in"], cap["groups"], c.window,
+                                      rows=rows)
+    t_rows = time.time() - t0
+    err = np.abs(cap["out_rows"] - o_ref)
+    lerr = np.abs(cap["lse_rows"] - l_ref)
+    t0 = time.time()
+    pair_checks = {}
+    for name, (groups, window, q0_pairs) in prefill.items():
+        exact = int(pair_count_ref(groups, window).sum())
+        pair_checks[name] = {"pair_count_ref": exact, "q0_run": q0_pairs, "equal": exact == q0_pairs}
+    t_pairs = time.time() - t0
+    checks = {
+        "assign_full_size": {"tokens": c.n, "unflagged_group_mismatches": unflagged,
+                             "tie_window_tokens": int(ref["tie"].sum()),
+                             "tie_window_mismatches": int((~same & ref["tie"]).sum()),
+                             "col_potential_max_abs_err": v_err},
+        "attention_rows": {"rows": int(len(rows)), "max_abs_err_out": float(err.max()),
+                           "mean_abs_err_out": float(err.mean()),
+                           "max_abs_err_lse": float(lerr.max())},
+        "allowed_pairs": pair_checks, "pair_count_s": t_pairs,
+    }
+    log(f"[bench] oracle checks: {json.dumps(checks)}")
+    assert unflagged == 0, "the timed step's groups differ from the oracle outside the tie window"
+    assert v_err <= 2e-5, "the timed step's column potential differs from the oracle"
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 1e-4, "attention rows differ"
+    assert all(x["equal"] for x in pair_checks.values()), "Q = 0 pair counts differ from the oracle"
+    tok_s = 1.0 / (t_assign / c.n + t_rows / len(rows))
     return {"value": tok_s, "unit": "tokens/s", "cores": cores, "blas_threads": threads,
             "kind": "oracle",
-            "sample": f"assign_ref on {n_a} tokens of the {c.name} shapes ({t_assign * n_a:.3f}s) "
-                      f"+ attention_rows_ref on {len(rows)} uniformly drawn rows of the full "
-                      f"{c.n}-token sequence ({t_rows:.1f}s); tokens/s = 1/(s/token + s/row)"}
+            "sample": f"assign_ref over all {c.n} tokens of the {c.name} step ({t_assign:.1f}s) + "
+                      f"attention_rows_ref on {len(rows)} stratified rows (first, last and uniform) "
+                      f"of the full sequence ({t_rows:.1f}s); tokens/s = 1/(s/token + s/row)",
+            "checks": checks}
 
 
 # ------------------------------------------------------------------ main
@@ -581,8 +629,15 @@ def main():
         calibration_copy()
     cfg = {x.name: x for x in CONFIGS}
     c3 = cfg["gqa70b_n128k"]
-    res3, st3 = prefill_bench(c3, args.steps, args.warmup, hip)
+    res3, st3 = prefill_bench(c3, args.steps, args.warmup, hip, capture=not args.no_cpu_baseline)
     extra = {}
+    prefill = {}  # workload -> (memberships, window, Q = 0 pair count), for the oracle leg
+
+    def keep(c, res):
+        prefill[c.name] = (res.pop("_groups"), c.window, res["allowed_pairs"])
+        return res
+    cap3 = res3.pop("_capture", None)
+    keep(c3, res3)
     if not args.quick:
         extra["dense_baseline_128k"] = dense_baseline(c3, st3, hip)
         extra["dense_baseline_128k"]["focus_speedup_vs_own_dense"] = (
@@ -594,9 +649,15 @@ def main():
     torch.cuda.empty_cache()
     if not args.quick:
         res4, st4 = prefill_bench(cfg["long_n1m"], max(3, args.steps // 2), 1, hip)
-        extra["long_n1m"] = res4
+        extra["long_n1m"] = keep(cfg["long_n1m"], res4)
         del st4
         torch.cuda.empty_cache()
+        # the two smaller prefill workloads (2K GPT-2-small-shaped MHA, 32K 7B-shaped GQA)
+        for name in ("gpt2s_n2k", "gqa7b_n32k"):
+            r, st = prefill_bench(cfg[name], max(args.steps, 20), args.warmup, hip)
+            extra[name] = keep(cfg[name], r)
+            del st
+            torch.cuda.empty_cache()
         extra["decode_b64_l64k"] = decode_bench(cfg["decode_b64_l64k"], 20, 3)
         torch.cuda.empty_cache()
     line = {
@@ -616,7 +677,7 @@ def main():
     line.update(extra)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(c3)
+        line["cpu_baseline"] = cpu_baseline(c3, cap3, prefill)
     print(json.dumps(line), flush=True)
 
 
