@@ -16,3 +16,11 @@ from .focus_ref import (  # noqa: F401
     soft_gate_ref,
     topk_ref,
 )
+from .train_ref import (  # noqa: F401
+    biased_attention_ref,
+    sinkhorn_iterates_ref,
+    soft_affinity_bias_ref,
+    soft_assignment_ref,
+    soft_train_backward_ref,
+    soft_train_forward_ref,
+)
