@@ -49,10 +49,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# ------------------------------------------------------------------ measured HBM traffic
+# ------------------------------------------------------------------ measured counters
 KERNEL_SRC = os.path.join(ROOT, "learned_centroid_gated_amd", "csrc", "attention_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "group_attention_gqa70b_n128k_traffic.md")
+COUNTER_FILES = {name: os.path.join(ROOT, "profiles", f"attention_counters_{name}.md")
+                 for name in ("gqa70b_n128k", "long_n1m")}
 CALIBRATION_BYTES = 1 << 30  # one fp32 negation over 2^28 elements reads and writes 1 GiB each
+FLOP_PER_CLOCK = 1024 * 1024  # bf16 MFMA flop per clock: 1024 per SIMD, 1024 SIMDs (256 CUs)
 
 
 def source_sha256(path):
@@ -61,21 +63,25 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the group-attention kernel, from the FETCH_SIZE/WRITE_SIZE
-    counter runs summarised in profiles/ (scaled by the same counters on a plain copy of
-    known size); None when the summary is absent or the kernel source changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_counters(workload):
+    """Per-pass figures of the attention kernels from the counter runs summarised in profiles/
+    (HBM bytes per launch from FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size, the
+    clock each pass ran at, MFMA busy); None when there is no summary for the workload or the
+    attention kernel source changed since the counters were taken."""
+    path = COUNTER_FILES.get(workload)
+    if not path or not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     if vals.get("source_sha256") != source_sha256(KERNEL_SRC):
         return None
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return {p: {"traffic": float(vals[f"{p}_traffic_bytes_per_launch"]),
+                    "clock_ghz": float(vals[f"{p}_clock_ghz"]),
+                    "mfma_busy": float(vals[f"{p}_mfma_busy"])} for p in ("group", "window")}
     except (KeyError, ValueError):
         return None
 
@@ -266,11 +272,24 @@ def prefill_bench(c, steps, warmup, hip, capture=False):
     if dom != "gather":
         p = gpairs if dom == "group_attention" else wpairs
         ach = flops_pair * p / (stage_ms[dom] * 1e-3) / 1e12
+        cnt = measured_counters(c.name)
+        pc = cnt["group" if dom == "group_attention" else "window"] if cnt else None
         res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                           "traffic": measured_traffic() if (dom == "group_attention" and
-                                                            c.name == "gqa70b_n128k") else None,
+                           "traffic": pc["traffic"] if pc else None,
                            "algorithmic_per_launch": flops_pair * p, "avg_launch_ms": stage_ms[dom]}
+        if pc:
+            # the same against the peak at the clock the pass actually ran at (counters)
+            peak_clk = FLOP_PER_CLOCK * pc["clock_ghz"] * 1e9 / 1e12
+            res["roofline"].update({"clock_ghz": pc["clock_ghz"], "peak_clock_derived": peak_clk,
+                                    "frac_clock_derived": ach / peak_clk,
+                                    "mfma_busy": pc["mfma_busy"]})
+        if cnt:
+            for pname, stage, pp in (("group", "group_attention", gpairs),
+                                     ("window", "window_attention_merge", wpairs)):
+                tf = flops_pair * pp / (stage_ms[stage] * 1e-3) / 1e12
+                peak_clk = FLOP_PER_CLOCK * cnt[pname]["clock_ghz"] * 1e9 / 1e12
+                res[f"{pname}_pct_clock_derived_peak"] = 100 * tf / peak_clk
     else:
         ach = gather_bytes / (stage_ms[dom] * 1e-3) / 1e9
         res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
@@ -610,6 +629,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--decode", action="store_true",
                     help="only the batched decode workload (prints its own JSON line)")
+    ap.add_argument("--workload", default=None,
+                    help="time one prefill workload only, e.g. long_n1m (prints its own JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB copy, to scale HBM byte counters")
@@ -628,6 +649,12 @@ def main():
     if args.calibrate_copy:
         calibration_copy()
     cfg = {x.name: x for x in CONFIGS}
+    if args.workload:
+        res, st = prefill_bench(cfg[args.workload], args.steps, args.warmup, hip)
+        res.pop("_groups")
+        del st
+        print(json.dumps(res), flush=True)
+        return
     c3 = cfg["gqa70b_n128k"]
     res3, st3 = prefill_bench(c3, args.steps, args.warmup, hip, capture=not args.no_cpu_baseline)
     extra = {}
