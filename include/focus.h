@@ -19,7 +19,8 @@
  *   - Pointers named as device buffers are device memory of the current HIP device, owned by
  *     the caller; the library never allocates, frees or retains them and keeps no state
  *     between calls. Scratch memory comes from the caller as `workspace`, sized by the
- *     matching *_workspace_size query.
+ *     matching *_workspace_size query (focus_decode_noalloc alone uses a fixed scratch array
+ *     inside the library instead; see there).
  *   - bf16 tensors, the fp32 inputs of focus_assign and every workspace must be 16-byte
  *     aligned; int32 buffers and fp32 lse / col_potential outputs 4-byte aligned (else
  *     FOCUS_ERR_ALIGN). Tensors are dense and row-major in the shapes given. bf16 tensors are
@@ -50,7 +51,8 @@ enum focus_status {
   FOCUS_ERR_UNSUPPORTED = -3,  /* a valid shape this build has no kernel for             */
   FOCUS_ERR_ALIGN = -4,        /* a device pointer that is not 16-byte aligned           */
   FOCUS_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than the size query returns  */
-  FOCUS_ERR_HIP = -6           /* the HIP runtime reported an error while enqueueing     */
+  FOCUS_ERR_HIP = -6,          /* the HIP runtime reported an error while enqueueing     */
+  FOCUS_ERR_SCRATCH = -7       /* needs more scratch than focus_decode_noalloc holds     */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -271,6 +273,31 @@ int focus_decode(const uint16_t* q, const int32_t* q_groups,
                  int K, int top_k, int64_t window, float scale,
                  uint16_t* out, float* lse,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * focus_decode_noalloc - focus_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ *
+ * Same arguments, checks, results and kernels as focus_decode, without the workspace: the
+ * scratch space lives in a fixed device array inside the library, one copy per GPU, of
+ * focus_decode_noalloc_scratch_bytes() bytes (64 MiB), held until the process ends. The call
+ * allocates and frees nothing. A call whose focus_decode_workspace_size(B, Lmax, Hq, Hkv,
+ * d_head, K, top_k) exceeds that size returns FOCUS_ERR_SCRATCH and enqueues nothing (the
+ * 64 x 65536-token decode with 32 query heads, d_head 128 and top_k 2 needs about 51 MB).
+ * The first call on a device looks up that device's copy (FOCUS_ERR_HIP if the lookup fails).
+ *
+ * Every call on one GPU shares that GPU's scratch, and each call rewrites what it reads, so
+ * calls need nothing cleared between them; but two calls that overlap in time on one GPU
+ * (different streams, or host threads) race on the scratch and must be serialised by the
+ * caller. Results are identical to focus_decode's on the same inputs.
+ * ------------------------------------------------------------------------------------ */
+size_t focus_decode_noalloc_scratch_bytes(void);
+int focus_decode_noalloc(const uint16_t* q, const int32_t* q_groups,
+                         const uint16_t* k_cache, const uint16_t* v_cache,
+                         const int32_t* cache_len, const int32_t* cache_groups,
+                         const int32_t* cache_offsets, const int32_t* cache_idx, int B,
+                         int64_t Lmax, int Hq, int Hkv, int d_head, int K, int top_k,
+                         int64_t window, float scale, uint16_t* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * focus_decode_paged - focus_decode over a paged KV cache (the paged cache that goes with

@@ -14,6 +14,7 @@ from .focus import (  # noqa: F401
     focus_bucket_append,
     focus_bucket_workspace_size,
     focus_decode,
+    focus_decode_noalloc,
     focus_decode_paged,
     focus_decode_slots,
     focus_slots_append,

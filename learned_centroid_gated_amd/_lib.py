@@ -42,6 +42,9 @@ SIGNATURES = {
                                    c_p, c_p, c_p, c_sz, c_p]),
     "focus_decode": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int, c_int,
                              c_int, c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p]),
+    "focus_decode_noalloc_scratch_bytes": (c_sz, []),
+    "focus_decode_noalloc": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int,
+                                     c_int, c_int, c_int, c_int, c_i64, c_f, c_p, c_p, c_p]),
 }
 
 _lib = None

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/focus.h"
 #include "focus_internal.hpp"
@@ -139,6 +140,68 @@ int resolve_scale(float scale, int d_head, float* out) {
 
 }  // namespace
 
+namespace {
+// Host-side checks of a focus_decode call apart from its workspace, in the order the entry
+// point reports them; fills the launch shape. A call with B == 0 passes with s->B == 0.
+int decode_check(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_cache,
+                 const uint16_t* v_cache, const int32_t* cache_len, const int32_t* cache_groups,
+                 const int32_t* cache_offsets, const int32_t* cache_idx, int B, int64_t Lmax,
+                 int Hq, int Hkv, int d_head, int K, int top_k, int64_t window, float scale,
+                 uint16_t* out, float* lse, DecodeShape* s) {
+  if (B < 0 || Lmax < 1 || window < 0) return FOCUS_ERR_ARG;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = check_groups(K, top_k, 4)) return st;
+  float sc;
+  if (int st = resolve_scale(scale, d_head, &sc)) return st;
+  if (Lmax * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
+  *s = DecodeShape{};
+  if (B == 0) return FOCUS_OK;
+  if (!q || !q_groups || !k_cache || !v_cache || !cache_len || !cache_groups || !cache_offsets ||
+      !cache_idx || !out || !lse)
+    return FOCUS_ERR_ARG;
+  if (!aligned16(q) || !aligned4(q_groups) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(cache_len) || !aligned4(cache_groups) || !aligned4(cache_offsets) ||
+      !aligned4(cache_idx) || !aligned16(out) || !aligned4(lse))
+    return FOCUS_ERR_ALIGN;
+  s->B = B;
+  s->Lmax = Lmax;
+  s->Hq = Hq;
+  s->Hkv = Hkv;
+  s->G = Hq / Hkv;
+  s->dh = d_head;
+  s->K = K;
+  s->top_k = top_k;
+  s->window = window;
+  s->scale = sc;
+  s->splits = decode_splits(*s);
+  return FOCUS_OK;
+}
+
+// ---------------------------------------------------------------- allocation-free decode
+// Scratch of focus_decode_noalloc: a file-scope device array, one copy per GPU the library runs
+// on, held until the process ends. In host code `scratch` names a host-side stand-in, not device
+// memory: kernels get the device address from hipGetSymbolAddress, taken once per device with
+// that device current and kept in scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+void* scratch_ptr[kMaxDevices] = {};
+std::mutex scratch_mutex;
+
+// The calling thread's current device's scratch address, or nullptr on a HIP error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 const char* focus_status_string(int status) {
@@ -150,6 +213,8 @@ const char* focus_status_string(int status) {
     case FOCUS_ERR_ALIGN: return "FOCUS_ERR_ALIGN: device pointer not 16-byte aligned";
     case FOCUS_ERR_WORKSPACE: return "FOCUS_ERR_WORKSPACE: workspace missing or too small";
     case FOCUS_ERR_HIP: return "FOCUS_ERR_HIP: HIP runtime error while enqueueing";
+    case FOCUS_ERR_SCRATCH:
+      return "FOCUS_ERR_SCRATCH: the call needs more scratch than the allocation-free entry point holds";
     default: return "FOCUS_ERR_UNKNOWN";
   }
 }
@@ -455,42 +520,51 @@ size_t focus_decode_workspace_size(int B, int64_t Lmax, int Hq, int Hkv, int d_h
   return decode_carve(nullptr, B, Lmax, Hq, d_head, top_k, decode_splits(s), nullptr);
 }
 
+
 int focus_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_cache,
                  const uint16_t* v_cache, const int32_t* cache_len, const int32_t* cache_groups,
                  const int32_t* cache_offsets, const int32_t* cache_idx, int B, int64_t Lmax,
                  int Hq, int Hkv, int d_head, int K, int top_k, int64_t window, float scale,
                  uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                  void* stream) {
-  if (B < 0 || Lmax < 1 || window < 0) return FOCUS_ERR_ARG;
-  if (int st = check_heads(Hq, Hkv, d_head)) return st;
-  if (int st = check_groups(K, top_k, 4)) return st;
-  float sc;
-  if (int st = resolve_scale(scale, d_head, &sc)) return st;
-  if (Lmax * (int64_t)top_k >= kIdxLimit) return FOCUS_ERR_SHAPE;
-  if (B == 0) return FOCUS_OK;
-  if (!q || !q_groups || !k_cache || !v_cache || !cache_len || !cache_groups || !cache_offsets ||
-      !cache_idx || !out || !lse)
-    return FOCUS_ERR_ARG;
-  if (!aligned16(q) || !aligned4(q_groups) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned4(cache_len) || !aligned4(cache_groups) || !aligned4(cache_offsets) ||
-      !aligned4(cache_idx) || !aligned16(out) || !aligned4(lse) || !aligned16(workspace))
-    return FOCUS_ERR_ALIGN;
+  DecodeShape s;
+  if (int st = decode_check(q, q_groups, k_cache, v_cache, cache_len, cache_groups, cache_offsets,
+                            cache_idx, B, Lmax, Hq, Hkv, d_head, K, top_k, window, scale, out, lse,
+                            &s))
+    return st;
+  if (s.B == 0) return FOCUS_OK;
+  if (!aligned16(workspace)) return FOCUS_ERR_ALIGN;
   const size_t need = focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k);
   if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
-  DecodeShape s{};
-  s.B = B;
-  s.Lmax = Lmax;
-  s.Hq = Hq;
-  s.Hkv = Hkv;
-  s.G = Hq / Hkv;
-  s.dh = d_head;
-  s.K = K;
-  s.top_k = top_k;
-  s.window = window;
-  s.scale = sc;
-  s.splits = decode_splits(s);
   DecodeWs w;
   decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
+                                  cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
+                                  w.part_ml, out, lse, (hipStream_t)stream));
+}
+
+size_t focus_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int focus_decode_noalloc(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int32_t* cache_len,
+                         const int32_t* cache_groups, const int32_t* cache_offsets,
+                         const int32_t* cache_idx, int B, int64_t Lmax, int Hq, int Hkv,
+                         int d_head, int K, int top_k, int64_t window, float scale,
+                         uint16_t* out, float* lse, void* stream) {
+  DecodeShape s;
+  if (int st = decode_check(q, q_groups, k_cache, v_cache, cache_len, cache_groups, cache_offsets,
+                            cache_idx, B, Lmax, Hq, Hkv, d_head, K, top_k, window, scale, out, lse,
+                            &s))
+    return st;
+  if (s.B == 0) return FOCUS_OK;
+  // every scratch byte the kernels read is written earlier in the same call, so nothing is
+  // cleared between calls
+  if (focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k) > kScratchBytes)
+    return FOCUS_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (!ws) return FOCUS_ERR_HIP;
+  DecodeWs w;
+  decode_carve(ws, B, Lmax, Hq, d_head, top_k, s.splits, &w);
   return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
                                   cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
                                   w.part_ml, out, lse, (hipStream_t)stream));

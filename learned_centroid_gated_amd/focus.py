@@ -357,6 +357,33 @@ def focus_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups, cache_o
     return out, lse
 
 
+def focus_decode_noalloc(q, q_groups, k_cache, v_cache, cache_len, cache_groups, cache_offsets,
+                         cache_idx, K, window, scale=0.0, out=None, lse=None, stream=None):
+    """focus_decode without a workspace: the library's fixed per-GPU scratch serves the call
+    (calls overlapping on one GPU race on it). Returns (out [B, Hq, dh] bf16, lse [B, Hq])."""
+    B, Hq, dh, top_k = _decode_query_shapes(q, q_groups, out, lse)
+    _, Lmax, Hkv, _ = _dims(k_cache, "k_cache", 4)
+    _shape(k_cache, "k_cache", (B, Lmax, Hkv, dh))
+    _shape(v_cache, "v_cache", (B, Lmax, Hkv, dh))
+    _shape(cache_len, "cache_len", (B,))
+    _shape(cache_groups, "cache_groups", (B, Lmax, top_k))
+    _numel(cache_offsets, "cache_offsets", B * (K + 1))
+    _numel(cache_idx, "cache_idx", B * Lmax * top_k)
+    dev = q.device
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, torch.bfloat16, dev)
+    for t, name in ((q_groups, "q_groups"), (cache_len, "cache_len"),
+                    (cache_groups, "cache_groups"), (cache_offsets, "cache_offsets"),
+                    (cache_idx, "cache_idx")):
+        _need(t, name, torch.int32, dev)
+    out, lse = _decode_outputs(B, Hq, dh, out, lse, dev)
+    _lib_call("focus_decode_noalloc", _ptr(q), _ptr(q_groups), _ptr(k_cache), _ptr(v_cache),
+              _ptr(cache_len), _ptr(cache_groups), _ptr(cache_offsets), _ptr(cache_idx), B, Lmax,
+              Hq, Hkv, dh, K, top_k, int(window), float(scale), _ptr(out), _ptr(lse),
+              _stream(stream))
+    return out, lse
+
+
 def _paged_shapes(q, k_pages, v_pages, page_table, cache_len, cache_groups, top_k, B, dh):
     num_pages, page_size, Hkv, _ = _dims(k_pages, "k_pages", 4)
     _shape(k_pages, "k_pages", (num_pages, page_size, Hkv, dh))

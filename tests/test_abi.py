@@ -35,14 +35,14 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
     assert lib.focus_version() >= 100
-    for code in (OK, ARG, SHAPE, UNSUP, ALIGN, WS, -6):
+    for code in (OK, ARG, SHAPE, UNSUP, ALIGN, WS, -6, -7):
         assert lib.focus_status_string(code).decode().startswith("FOCUS_")
     assert b"UNKNOWN" in lib.focus_status_string(-99)
 
@@ -306,3 +306,29 @@ def test_decode_slots_validation(lib):
     assert _dslots(lib, ws=None) == WS
     assert _dslots(lib, wsb=16) == WS
     assert _dslots(lib, B=0, q=None) == OK
+
+
+def _noalloc(lib, q=P, qg=P, kc=P, vc=P, ln=P, cg=P, co=P, ci=P, B=4, L=1024, Hq=8, Hkv=2,
+             dh=128, K=16, top_k=2, window=64, scale=0.0, out=P, lse=P):
+    return lib.focus_decode_noalloc(q, qg, kc, vc, ln, cg, co, ci, B, L, Hq, Hkv, dh, K, top_k,
+                                    window, scale, out, lse, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode refuses what focus_decode refuses, and every call whose
+    scratch would exceed the fixed array, before touching the device."""
+    cap = lib.focus_decode_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    assert _noalloc(lib, B=-1) == ARG
+    assert _noalloc(lib, L=0) == ARG
+    assert _noalloc(lib, dh=32) == UNSUP
+    assert _noalloc(lib, top_k=5) == UNSUP
+    assert _noalloc(lib, L=1 << 31, top_k=1) == SHAPE
+    for name in ("q", "qg", "kc", "vc", "ln", "cg", "co", "ci", "out", "lse"):
+        assert _noalloc(lib, **{name: None}) == ARG, name
+    assert _noalloc(lib, ci=MIS) == ALIGN
+    assert _noalloc(lib, B=0, q=None) == OK
+    # the 64 x 65536 decode fits; twice the sequences do not
+    ws = lib.focus_decode_workspace_size
+    assert ws(64, 65536, 32, 8, 128, 64, 2) <= cap < ws(128, 65536, 32, 8, 128, 64, 2)
+    assert _noalloc(lib, B=128, L=65536, Hq=32, Hkv=8, K=64) == -7
