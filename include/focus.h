@@ -243,6 +243,54 @@ int focus_soft_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          float scale, uint16_t* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Soft-gated training: the forward over every causal pair and the backward that trains only
+ * the centroids and the projection (Dutch technical summary, Kerncomponenten 1, 2 and 4: the
+ * soft assignment g_i, Sinkhorn balancing during training, soft gates on every pair; Chinese
+ * technical summary, section 2.1.2 gate formula and section 2.2: only the centroids and the
+ * projection are trained, the model stays frozen).
+ *
+ *   S = (hidden * w_g) * centroids^T; T = sinkhorn_iters log-domain Sinkhorn iterations as in
+ *   focus_assign; g = exp(S + u + v) (the balanced plan, one row per token; T = 0: g = exp(S))
+ *   a_ij       = g_i . g_j - 1/2                                  (group affinity)
+ *   logit_ij   = scale * q[i,h] . k[j,h/G] + (i - j >= window ? log sigmoid(lambda * a_ij) : 0)
+ *   out[i, h]  = sum over j <= i of softmax_j(logit_ij) * v[j,h/G];   lse as in focus_attention
+ *
+ * focus_soft_train_forward writes out and lse. focus_soft_train_backward takes them with the
+ * upstream gradient dout = dL/dout and writes dL/dcentroids, dL/dw_g and, when d_hidden is not
+ * NULL, dL/dhidden (q, k, v are inputs of the frozen model: no gradient). With one-hot rows g,
+ * a_ij is the shared-group indicator minus 1/2 and the forward is focus_soft_attention's.
+ *
+ *   hidden, w_g, centroids, n, d, d_g, K, sinkhorn_iters   as for focus_assign, with
+ *            K <= 128 (FOCUS_ERR_UNSUPPORTED above) and sinkhorn_iters <= 64.
+ *   q, k, v, Hq, Hkv, d_head, scale, out, lse   as for focus_attention (out bf16 [n, Hq, d_head],
+ *            lse fp32 [n, Hq]).
+ *   window   >= 0: pairs with i - j < window carry no gate.
+ *   lambda   finite gate sharpness.
+ *   dout     device, [n, Hq, d_head] bf16.
+ *   d_centroids  device, out [K, d_g] fp32;  d_w_g  device, out [d, d_g] fp32;
+ *   d_hidden     device, out [n, d] fp32, or NULL.
+ *   workspace    at least focus_soft_train_workspace_size(n, d, d_g, K, Hq, sinkhorn_iters)
+ *            bytes (the same size serves both calls).
+ * The gradients are accumulated with atomic adds, so their last bits may differ between runs.
+ * Dense causal cost: every pair j <= i is computed (the backward visits only far pairs).
+ * ------------------------------------------------------------------------------------ */
+size_t focus_soft_train_workspace_size(int64_t n, int d, int d_g, int K, int Hq,
+                                       int sinkhorn_iters);
+int focus_soft_train_forward(const float* hidden, const float* w_g, const float* centroids,
+                             int64_t n, int d, int d_g, int K, int sinkhorn_iters,
+                             const uint16_t* q, const uint16_t* k, const uint16_t* v, int Hq,
+                             int Hkv, int d_head, int64_t window, float lambda, float scale,
+                             uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
+int focus_soft_train_backward(const float* hidden, const float* w_g, const float* centroids,
+                              int64_t n, int d, int d_g, int K, int sinkhorn_iters,
+                              const uint16_t* q, const uint16_t* k, const uint16_t* v, int Hq,
+                              int Hkv, int d_head, int64_t window, float lambda, float scale,
+                              const uint16_t* out, const float* lse, const uint16_t* dout,
+                              float* d_centroids, float* d_w_g, float* d_hidden, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * focus_decode - one new token per sequence against its own cache (ZH 2.1.3 inference).
  *
  * Sequence b holds L_b = cache_len[b] tokens; its new token is the last one, at position

@@ -21,5 +21,8 @@ from .focus import (  # noqa: F401
     focus_slots_from_bucket,
     focus_decode_workspace_size,
     focus_soft_attention,
+    focus_soft_train_backward,
+    focus_soft_train_forward,
+    focus_soft_train_workspace_size,
 )
 from ._lib import LIB_PATH, FocusError, lib, status_string  # noqa: F401

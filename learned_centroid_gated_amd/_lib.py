@@ -42,6 +42,13 @@ SIGNATURES = {
                                    c_p, c_p, c_p, c_sz, c_p]),
     "focus_decode": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int, c_int,
                              c_int, c_int, c_int, c_i64, c_f, c_p, c_p, c_p, c_sz, c_p]),
+    "focus_soft_train_workspace_size": (c_sz, [c_i64, c_int, c_int, c_int, c_int, c_int]),
+    "focus_soft_train_forward": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_int, c_p,
+                                         c_p, c_p, c_int, c_int, c_int, c_i64, c_f, c_f, c_p, c_p,
+                                         c_p, c_sz, c_p]),
+    "focus_soft_train_backward": (c_int, [c_p, c_p, c_p, c_i64, c_int, c_int, c_int, c_int, c_p,
+                                          c_p, c_p, c_int, c_int, c_int, c_i64, c_f, c_f, c_p,
+                                          c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "focus_decode_noalloc_scratch_bytes": (c_sz, []),
     "focus_decode_noalloc": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_i64, c_int,
                                      c_int, c_int, c_int, c_int, c_i64, c_f, c_p, c_p, c_p]),

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libfocus.so")
 ARCH = "gfx950"
 
 SOURCES = ["focus_api.hip", "assign_kernels.hip", "bucket_kernels.hip", "attention_kernels.hip",
-           "decode_kernels.hip"]
+           "decode_kernels.hip", "train_kernels.hip"]
 
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

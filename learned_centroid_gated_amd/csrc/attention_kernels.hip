@@ -253,15 +253,7 @@ struct FlashArgs {
 constexpr int KT = 64;  // keys per kv tile
 
 // K and V tiles live in LDS row-major, 2*DH bytes per key row, with the 16-byte chunks of row r
-// permuted by chunk ^ swz(r). swz maps the 16 rows of a block to 16 distinct values whose
-// even parts differ across any 4 consecutive rows, so both access patterns are free of bank
-// conflicts: 16 lanes reading one chunk of 16 consecutive rows (K as the MFMA A operand) and
-// 16 lanes reading 2 adjacent chunks of 4 consecutive rows (V through the transposing read).
-// swz depends on the low 4 bits of the row only, so rows 16 apart share a permutation and every
-// lane's LDS addresses differ between tiles and row blocks by compile-time constants.
-__device__ __forceinline__ int swz(int row) {
-  return ((row & 1) << 3) | (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
-}
+// permuted by chunk ^ swz(r) (swz in focus_internal.hpp).
 
 // Ownership bias rows (group pass, MKS > 0): mrow[j][key][t] is bf16 1.0 when the key shares a
 // lower group with query token 16 j + t of the tile, else 0. One extra MFMA k-step per 16

@@ -482,6 +482,188 @@ int focus_soft_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
                                           (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// ============================================================================ soft-gated training
+// Workspace of the training path: the score products (W_g^T, the product operand's bf16 planes, Z,
+// S), every Sinkhorn column potential v^0..v^T, the column partials, the soft assignment's two
+// bf16 planes; and for the backward the rowwise dO . O, dG, dS, du, the backward column partials,
+// two potential gradients and dZ.
+struct TrainWs {
+  float *Bt, *Z, *S, *vs;
+  __bf16* Bp;
+  float2* partials;
+  __bf16 *gh, *gl;
+  float *D, *dG, *dS, *du, *part, *dv, *dZ;
+};
+
+inline int train_groups_padded(int K) { return (K + 31) / 32 * 32; }
+
+size_t train_carve(void* ws, int64_t n, int d, int d_g, int K, int Hq, int iters, TrainWs* out) {
+  Carver c(ws);
+  TrainWs w{};
+  const int K4 = padded_k(K), KP = train_groups_padded(K);
+  w.Bt = c.take<float>((size_t)d_g * d);
+  w.Bp = c.take<__bf16>(3 * std::max((size_t)d_g * d, (size_t)K * d_g));
+  w.Z = c.take<float>((size_t)n * d_g);
+  w.S = c.take<float>((size_t)n * K4);
+  w.vs = c.take<float>((size_t)(iters + 1) * K4);
+  w.partials = c.take<float2>((size_t)sinkhorn_blocks(n, K) * K);
+  w.gh = c.take<__bf16>((size_t)n * KP);
+  w.gl = c.take<__bf16>((size_t)n * KP);
+  w.D = c.take<float>((size_t)n * Hq);
+  w.dG = c.take<float>((size_t)n * K);
+  w.dS = c.take<float>((size_t)n * K);
+  w.du = c.take<float>((size_t)n);
+  w.part = c.take<float>((size_t)train_sk_blocks(n) * K);
+  w.dv = c.take<float>((size_t)2 * K4);
+  w.dZ = c.take<float>((size_t)n * d_g);
+  if (out) *out = w;
+  return c.used;
+}
+
+// Checks shared by the training forward and backward, in the order they report.
+int train_check(const float* hidden, const float* w_g, const float* centroids, int64_t n, int d,
+                int d_g, int K, int sinkhorn_iters, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, int Hq, int Hkv, int d_head, int64_t window, float lambda,
+                float scale, float* sc) {
+  if (n < 0 || d < 1 || d_g < 1 || d_g > 1024 || sinkhorn_iters < 0 || sinkhorn_iters > 64 ||
+      window < 0 || isnan(lambda) || isinf(lambda))
+    return FOCUS_ERR_ARG;
+  if (K < 1 || K > 1024) return FOCUS_ERR_ARG;
+  if (K > 128 || d % 4 != 0 || d_g % 4 != 0) return FOCUS_ERR_UNSUPPORTED;
+  if (int st = check_heads(Hq, Hkv, d_head)) return st;
+  if (int st = resolve_scale(scale, d_head, sc)) return st;
+  if (n * (int64_t)std::max(Hq, K) >= kIdxLimit || n * (int64_t)d >= ((int64_t)1 << 40))
+    return FOCUS_ERR_SHAPE;
+  if (n == 0) return FOCUS_OK;
+  if (!hidden || !w_g || !centroids || !q || !k || !v) return FOCUS_ERR_ARG;
+  if (!aligned16(hidden) || !aligned16(w_g) || !aligned16(centroids) || !aligned16(q) ||
+      !aligned16(k) || !aligned16(v))
+    return FOCUS_ERR_ALIGN;
+  return FOCUS_OK;
+}
+
+// Scores, every Sinkhorn iterate and the soft assignment's planes, as the forward computes them.
+hipError_t train_assign(const float* hidden, const float* w_g, const float* centroids, int64_t n,
+                        int d, int d_g, int K, int iters, const TrainWs& w, hipStream_t st) {
+  const int K4 = padded_k(K), KP = train_groups_padded(K);
+  auto product = [&](const float* a, const float* b, float* c, int64_t m, int nn, int kd,
+                     int ldc) -> hipError_t {
+    if (kd % 32 != 0) return launch_gemm_nt_f32(a, b, c, m, nn, kd, ldc, st);
+    hipError_t e2 = launch_split_planes(b, (int64_t)nn * kd, w.Bp, st);
+    if (e2 != hipSuccess) return e2;
+    return launch_gemm_nt_f32_planes(a, w.Bp, c, m, nn, kd, ldc, st);
+  };
+  // Z = H W_g (kept for the centroid gradient), S = Z C^T
+  hipError_t e = launch_transpose_f32(w_g, w.Bt, d, d_g, st);
+  if (e == hipSuccess) e = product(hidden, w.Bt, w.Z, n, d_g, d, d_g);
+  if (e == hipSuccess) e = product(w.Z, centroids, w.S, n, K, d_g, K4);
+  if (e == hipSuccess) e = launch_fill_f32(w.vs, 0.f, K4, st);
+  const int nblk = sinkhorn_blocks(n, K);
+  for (int t = 1; t <= iters && e == hipSuccess; ++t) {
+    e = hipMemcpyAsync(w.vs + (size_t)t * K4, w.vs + (size_t)(t - 1) * K4, sizeof(float) * K4,
+                       hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = launch_sinkhorn_iter(w.S, n, K, K4, w.vs + (size_t)t * K4, w.partials,
+                                                  nblk, st);
+  }
+  const float* vprev = w.vs + (size_t)(iters > 0 ? iters - 1 : 0) * K4;
+  const float* vlast = w.vs + (size_t)iters * K4;
+  if (e == hipSuccess)
+    e = launch_train_plan(w.S, n, K, K4, KP, vprev, vlast, iters, w.gh, w.gl, st);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t focus_soft_train_workspace_size(int64_t n, int d, int d_g, int K, int Hq,
+                                       int sinkhorn_iters) {
+  if (n < 0 || d < 1 || d_g < 1 || K < 1 || Hq < 1 || sinkhorn_iters < 0) return 0;
+  return train_carve(nullptr, n, d, d_g, K, Hq, sinkhorn_iters, nullptr);
+}
+
+int focus_soft_train_forward(const float* hidden, const float* w_g, const float* centroids,
+                             int64_t n, int d, int d_g, int K, int sinkhorn_iters,
+                             const uint16_t* q, const uint16_t* k, const uint16_t* v, int Hq,
+                             int Hkv, int d_head, int64_t window, float lambda, float scale,
+                             uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  float sc;
+  if (int st = train_check(hidden, w_g, centroids, n, d, d_g, K, sinkhorn_iters, q, k, v, Hq, Hkv,
+                           d_head, window, lambda, scale, &sc))
+    return st;
+  if (n == 0) return FOCUS_OK;
+  if (!out || !lse) return FOCUS_ERR_ARG;
+  if (!aligned16(out) || !aligned4(lse) || !aligned16(workspace)) return FOCUS_ERR_ALIGN;
+  TrainWs w;
+  const size_t need = train_carve(workspace, n, d, d_g, K, Hq, sinkhorn_iters, &w);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = train_assign(hidden, w_g, centroids, n, d, d_g, K, sinkhorn_iters, w, st);
+  TrainShape s{n, Hq, Hkv, d_head, K, train_groups_padded(K), window, sc, lambda};
+  if (e == hipSuccess) e = launch_train_attention(s, q, k, v, w.gh, w.gl, out, lse, st);
+  return hip_status(e);
+}
+
+int focus_soft_train_backward(const float* hidden, const float* w_g, const float* centroids,
+                              int64_t n, int d, int d_g, int K, int sinkhorn_iters,
+                              const uint16_t* q, const uint16_t* k, const uint16_t* v, int Hq,
+                              int Hkv, int d_head, int64_t window, float lambda, float scale,
+                              const uint16_t* out, const float* lse, const uint16_t* dout,
+                              float* d_centroids, float* d_w_g, float* d_hidden, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  float sc;
+  if (int st = train_check(hidden, w_g, centroids, n, d, d_g, K, sinkhorn_iters, q, k, v, Hq, Hkv,
+                           d_head, window, lambda, scale, &sc))
+    return st;
+  if (!d_centroids || !d_w_g) return FOCUS_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (n == 0) {  // empty sequence: zero gradients
+    hipError_t e = launch_fill_f32(d_centroids, 0.f, (int64_t)K * d_g, st);
+    if (e == hipSuccess) e = launch_fill_f32(d_w_g, 0.f, (int64_t)d * d_g, st);
+    return hip_status(e);
+  }
+  if (!out || !lse || !dout) return FOCUS_ERR_ARG;
+  if (!aligned16(out) || !aligned4(lse) || !aligned16(dout) || !aligned4(d_centroids) ||
+      !aligned4(d_w_g) || !aligned4(d_hidden) || !aligned16(workspace))
+    return FOCUS_ERR_ALIGN;
+  TrainWs w;
+  const size_t need = train_carve(workspace, n, d, d_g, K, Hq, sinkhorn_iters, &w);
+  if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
+  const int K4 = padded_k(K), T = sinkhorn_iters;
+  hipError_t e = train_assign(hidden, w_g, centroids, n, d, d_g, K, T, w, st);
+  TrainShape s{n, Hq, Hkv, d_head, K, train_groups_padded(K), window, sc, lambda};
+  // attention: dG = dL/dg from every far pair, both sides
+  if (e == hipSuccess) e = launch_train_delta(dout, out, n * Hq, d_head, w.D, st);
+  if (e == hipSuccess) e = launch_fill_f32(w.dG, 0.f, n * K, st);
+  if (e == hipSuccess)
+    e = launch_train_attention_bwd(s, q, k, v, w.gh, w.gl, lse, dout, w.D, w.dG, st);
+  // the plan exp(S + u^T + v^T), then every Sinkhorn iteration in reverse
+  const float* vprev = w.vs + (size_t)(T > 0 ? T - 1 : 0) * K4;
+  float* dv_cur = w.dv;
+  float* dv_next = w.dv + K4;
+  if (e == hipSuccess)
+    e = launch_train_sk_plan_bwd(w.S, n, K, K4, vprev, w.vs + (size_t)T * K4, T, w.dG, w.dS, w.du,
+                                 w.part, dv_cur, st);
+  for (int t = T; t >= 1 && e == hipSuccess; --t) {
+    e = launch_train_sk_iter_bwd(w.S, n, K, K4, w.vs + (size_t)(t - 1) * K4, w.vs + (size_t)t * K4,
+                                 dv_cur, t == T ? w.du : nullptr, w.dS, w.part, dv_next, st);
+    std::swap(dv_cur, dv_next);
+  }
+  // S = Z C^T, Z = H W_g
+  if (e == hipSuccess) e = launch_train_dz(w.dS, centroids, n, K, d_g, w.dZ, st);
+  if (e == hipSuccess) e = launch_fill_f32(d_centroids, 0.f, (int64_t)K * d_g, st);
+  if (e == hipSuccess) e = launch_gemm_tn_atomic(w.dS, w.Z, n, K, d_g, d_centroids, st);
+  if (e == hipSuccess) e = launch_fill_f32(d_w_g, 0.f, (int64_t)d * d_g, st);
+  if (e == hipSuccess) e = launch_gemm_tn_atomic(hidden, w.dZ, n, d, d_g, d_w_g, st);
+  if (e == hipSuccess && d_hidden) e = launch_gemm_nt_f32(w.dZ, w_g, d_hidden, n, d, d_g, d, st);
+  return hip_status(e);
+}
+
 int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int Hq,
                     int Hkv, int d_head, const int32_t* groups, const int32_t* offsets,
                     const int32_t* idx, const int32_t* slot, int K, int top_k, int64_t window,

@@ -83,14 +83,23 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 // whole copy before the first LDS read that follows, which serialises the prefetch of the next
 // tile with the compute on the current one. The caller waits (vmcnt) before the data is read.
 // The LDS destination goes in as a pointer operand (not an integer), so the compiler keeps
-// treating the buffer as written by the asm statement; m0 is listed as clobbered, since the
-// statement overwrites it with that destination.
+// treating the buffer as written by the asm statement. The instruction takes it in m0; the
+// operand is constrained to m0, so the compiler itself loads m0 before the statement and never
+// assumes m0 still holds an earlier value.
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, void* lds_dst) {
   lds_char_t* m = (lds_char_t*)lds_dst;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(m) : "memory");
+}
+
+// Tiles of bf16 rows in LDS keep each row's 16-byte chunks permuted by chunk ^ swz(row) (taken
+// modulo the chunks per row). swz maps the 16 rows of a block to 16 distinct values whose even
+// parts differ across any 4 consecutive rows, so both access patterns of a 256-byte-row tile are
+// free of bank conflicts: 16 lanes reading one chunk of 16 consecutive rows (an MFMA operand read
+// along the row) and 16 lanes reading 2 adjacent chunks of 4 consecutive rows (the transposing
+// read). swz depends on the low 4 bits of the row only, so rows 16 apart share a permutation and
+// every lane's LDS addresses differ between tiles and row blocks by compile-time constants.
+__device__ __forceinline__ int swz(int row) {
+  return ((row & 1) << 3) | (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
 }
 
 // s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt at their maxima)
@@ -185,6 +194,47 @@ hipError_t launch_soft_attention(const uint16_t* q, const uint16_t* k, const uin
                                  const int32_t* groups, const AttnShape& s, float bias_none,
                                  float bias_share, uint16_t* out, float* lse, hipStream_t stream);
 int attn_tile_tokens(int G);  // query tokens per attention tile: 128 / G
+
+// Soft-gated training path (train_kernels.hip).
+struct TrainShape {
+  int64_t n;
+  int Hq, Hkv, dh, K;
+  int KP;         // groups padded to a multiple of 32 (the soft-assignment planes' row length)
+  int64_t window;
+  float scale;    // natural-units logit scale
+  float lam;      // gate sharpness lambda
+};
+// Soft assignment g = exp(S + u + vlast), u from vprev (the last row step; iters == 0: g =
+// exp(S)), written as two bf16 planes gh, gl [n, KP] (zero past K).
+hipError_t launch_train_plan(const float* S, int64_t n, int K, int ldS, int KP, const float* vprev,
+                             const float* vlast, int iters, __bf16* gh, __bf16* gl,
+                             hipStream_t stream);
+// D[row] = dout[row] . out[row] over rows of dh bf16 values.
+hipError_t launch_train_delta(const uint16_t* dout, const uint16_t* out, int64_t rows, int dh,
+                              float* D, hipStream_t stream);
+// Forward over every causal pair, far pairs gated by log sigmoid(lam (g_i . g_j - 1/2)).
+hipError_t launch_train_attention(const TrainShape& s, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const __bf16* gh, const __bf16* gl,
+                                  uint16_t* out, float* lse, hipStream_t stream);
+// dG [n, K] += dL/dg from both sides of every far pair (dG zeroed by the caller).
+hipError_t launch_train_attention_bwd(const TrainShape& s, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const __bf16* gh, const __bf16* gl,
+                                      const float* lse, const uint16_t* dout, const float* D,
+                                      float* dG, hipStream_t stream);
+// Sinkhorn backward: the plan's row pass (dS = dG o P, du, dv = column sums), then one call per
+// iteration in reverse (dS -= ..., dvprev = -column sums of du o Wr). part: train_sk_blocks(n) x K.
+int train_sk_blocks(int64_t n);
+hipError_t launch_train_sk_plan_bwd(const float* S, int64_t n, int K, int ldS, const float* vprev,
+                                    const float* vlast, int iters, const float* dG, float* dS,
+                                    float* du, float* part, float* dv, hipStream_t stream);
+hipError_t launch_train_sk_iter_bwd(const float* S, int64_t n, int K, int ldS, const float* vprev,
+                                    const float* vcur, const float* dvcur, const float* du_in,
+                                    float* dS, float* part, float* dvprev, hipStream_t stream);
+// dZ = dS C ([n, K] x [K, dg]); C[M, N] += A^T B over R rows (A [R, M], B [R, N]).
+hipError_t launch_train_dz(const float* dS, const float* C, int64_t n, int K, int dg, float* dZ,
+                           hipStream_t stream);
+hipError_t launch_gemm_tn_atomic(const float* A, const float* B, int64_t R, int M, int N, float* C,
+                                 hipStream_t stream);
 
 // Decode.
 struct DecodeShape {

@@ -306,6 +306,89 @@ def focus_soft_attention(q, k, v, groups, K, window, lam, scale=0.0, out=None, l
     return out, lse
 
 
+# ------------------------------------------------------------------ soft-gated training
+def focus_soft_train_workspace_size(n, d, d_g, K, Hq, sinkhorn_iters):
+    return _lib.lib().focus_soft_train_workspace_size(n, d, d_g, K, Hq, sinkhorn_iters)
+
+
+def _train_shapes(hidden, w_g, centroids, q, k, v):
+    n, d = _dims(hidden, "hidden", 2)
+    _, d_g = _dims(w_g, "w_g", 2)
+    K, _ = _dims(centroids, "centroids", 2)
+    _shape(w_g, "w_g", (d, d_g))
+    _shape(centroids, "centroids", (K, d_g))
+    nq, Hq, Hkv, dh = _qkv_shapes(q, k, v)
+    if nq != n:
+        raise ValueError(f"q has {nq} tokens, hidden has {n}")
+    return n, d, d_g, K, Hq, Hkv, dh
+
+
+def _train_need(hidden, w_g, centroids, q, k, v):
+    dev = hidden.device
+    for t, name in ((hidden, "hidden"), (w_g, "w_g"), (centroids, "centroids")):
+        _need(t, name, torch.float32, dev)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, dev)
+    return dev
+
+
+def focus_soft_train_forward(hidden, w_g, centroids, sinkhorn_iters, q, k, v, window, lam,
+                             scale=0.0, out=None, lse=None, workspace=None, stream=None):
+    """Soft-gated training forward over every causal pair, the gate driven by the soft
+    assignment (the balanced Sinkhorn plan): returns (out [n, Hq, dh] bf16, lse [n, Hq])."""
+    n, d, d_g, K, Hq, Hkv, dh = _train_shapes(hidden, w_g, centroids, q, k, v)
+    _shape(out, "out", (n, Hq, dh))
+    _shape(lse, "lse", (n, Hq))
+    dev = _train_need(hidden, w_g, centroids, q, k, v)
+    _need_opt(out, "out", torch.bfloat16, dev)
+    _need_opt(lse, "lse", torch.float32, dev)
+    if out is None:
+        out = torch.empty((n, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((n, Hq), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_soft_train_workspace_size(n, d, d_g, K, Hq, sinkhorn_iters), dev,
+                    workspace)
+    _lib_call("focus_soft_train_forward", _ptr(hidden), _ptr(w_g), _ptr(centroids), n, d, d_g, K,
+              sinkhorn_iters, _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, dh, int(window), float(lam),
+              float(scale), _ptr(out), _ptr(lse), _ptr(ws), _ws_bytes(ws), _stream(stream))
+    return out, lse
+
+
+def focus_soft_train_backward(hidden, w_g, centroids, sinkhorn_iters, q, k, v, out, lse, dout,
+                              window, lam, scale=0.0, want_hidden=False, d_centroids=None,
+                              d_w_g=None, d_hidden=None, workspace=None, stream=None):
+    """Gradients of the soft-gated forward with respect to the centroids, the projection and
+    (want_hidden or d_hidden given) the hidden states, from the forward's out and lse and the
+    upstream gradient dout: returns (d_centroids [K, d_g], d_w_g [d, d_g], d_hidden or None)."""
+    n, d, d_g, K, Hq, Hkv, dh = _train_shapes(hidden, w_g, centroids, q, k, v)
+    for t, name, shape in ((out, "out", (n, Hq, dh)), (lse, "lse", (n, Hq)),
+                           (dout, "dout", (n, Hq, dh))):
+        _tensor(t, name)
+        _shape(t, name, shape)
+    _shape(d_centroids, "d_centroids", (K, d_g))
+    _shape(d_w_g, "d_w_g", (d, d_g))
+    _shape(d_hidden, "d_hidden", (n, d))
+    dev = _train_need(hidden, w_g, centroids, q, k, v)
+    _need(out, "out", torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _need(dout, "dout", torch.bfloat16, dev)
+    for t, name in ((d_centroids, "d_centroids"), (d_w_g, "d_w_g"), (d_hidden, "d_hidden")):
+        _need_opt(t, name, torch.float32, dev)
+    if d_centroids is None:
+        d_centroids = torch.empty((K, d_g), dtype=torch.float32, device=dev)
+    if d_w_g is None:
+        d_w_g = torch.empty((d, d_g), dtype=torch.float32, device=dev)
+    if d_hidden is None and want_hidden:
+        d_hidden = torch.empty((n, d), dtype=torch.float32, device=dev)
+    ws = _workspace(focus_soft_train_workspace_size(n, d, d_g, K, Hq, sinkhorn_iters), dev,
+                    workspace)
+    _lib_call("focus_soft_train_backward", _ptr(hidden), _ptr(w_g), _ptr(centroids), n, d, d_g,
+              K, sinkhorn_iters, _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, dh, int(window), float(lam),
+              float(scale), _ptr(out), _ptr(lse), _ptr(dout), _ptr(d_centroids), _ptr(d_w_g),
+              _ptr(d_hidden), _ptr(ws), _ws_bytes(ws), _stream(stream))
+    return d_centroids, d_w_g, d_hidden
+
+
 # ------------------------------------------------------------------ focus_decode
 def focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k):
     return _lib.lib().focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k)

@@ -23,4 +23,5 @@ from .train_ref import (  # noqa: F401
     soft_assignment_ref,
     soft_train_backward_ref,
     soft_train_forward_ref,
+    soft_train_forward_rows_ref,
 )

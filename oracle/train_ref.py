@@ -159,3 +159,28 @@ def soft_train_backward_ref(hidden, w_g, centroids, iters, q, k, v, dout, window
     dZ = dS @ C
     return dict(d_centroids=dS.T @ Z, d_w_g=H.T @ dZ, d_hidden=dZ @ W.T, d_plan=dP,
                 d_scores=dS)
+
+
+def soft_train_forward_rows_ref(g, q, k, v, window, lam, rows, scale=None):
+    """soft_train_forward_ref's output on the given query rows only, from the soft assignment g
+    (soft_assignment_ref): each row's gate biases are formed on their own, so long sequences can
+    be checked on a sample of rows. Returns (out [len(rows), Hq, dh], lse [len(rows), Hq])."""
+    g = np.asarray(g, np.float64)
+    n, Hq, dh = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(dh) if scale is None or scale <= 0 else float(scale)
+    out = np.empty((len(rows), Hq, v.shape[2]))
+    lse = np.empty((len(rows), Hq))
+    for r, i in enumerate(rows):
+        i = int(i)
+        j = np.arange(i + 1)
+        a = g[:i + 1] @ g[i] - 0.5
+        bias = np.where((i - j) >= window, -np.logaddexp(0.0, -lam * a), 0.0)
+        qi = _widen(q[i])
+        for h in range(Hq):
+            kk = _widen(k[:i + 1, h // G, :])
+            s = scale * kk @ qi[h] + bias
+            l = _logsumexp(s, axis=0)
+            out[r, h] = np.exp(s - l) @ _widen(v[:i + 1, h // G, :])
+            lse[r, h] = l
+    return out, lse

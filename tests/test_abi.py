@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 24, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -332,3 +332,65 @@ def test_decode_noalloc_validation(lib):
     ws = lib.focus_decode_workspace_size
     assert ws(64, 65536, 32, 8, 128, 64, 2) <= cap < ws(128, 65536, 32, 8, 128, 64, 2)
     assert _noalloc(lib, B=128, L=65536, Hq=32, Hkv=8, K=64) == -7
+
+
+def _train_args(**over):
+    a = dict(h=P, w=P, c=P, n=256, d=64, dg=16, K=8, iters=2, q=P, k=P, v=P, Hq=8, Hkv=2, dh=128,
+             window=16, lam=4.0, scale=0.0)
+    a.update(over)
+    return a
+
+
+def _train_fwd(lib, out=P, lse=P, ws=P, wsb=BIG, **over):
+    a = _train_args(**over)
+    return lib.focus_soft_train_forward(a["h"], a["w"], a["c"], a["n"], a["d"], a["dg"], a["K"],
+                                        a["iters"], a["q"], a["k"], a["v"], a["Hq"], a["Hkv"],
+                                        a["dh"], a["window"], a["lam"], a["scale"], out, lse, ws,
+                                        wsb, None)
+
+
+def _train_bwd(lib, out=P, lse=P, dout=P, dc=P, dw=P, dh_out=P, ws=P, wsb=BIG, **over):
+    a = _train_args(**over)
+    return lib.focus_soft_train_backward(a["h"], a["w"], a["c"], a["n"], a["d"], a["dg"], a["K"],
+                                         a["iters"], a["q"], a["k"], a["v"], a["Hq"], a["Hkv"],
+                                         a["dh"], a["window"], a["lam"], a["scale"], out, lse,
+                                         dout, dc, dw, dh_out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("call", [_train_fwd, _train_bwd])
+def test_soft_train_validation(lib, call):
+    assert call(lib, n=-1) == ARG
+    assert call(lib, window=-1) == ARG
+    assert call(lib, iters=-1) == ARG
+    assert call(lib, iters=65) == ARG
+    assert call(lib, lam=math.nan) == ARG
+    assert call(lib, lam=math.inf) == ARG
+    assert call(lib, scale=math.nan) == ARG
+    assert call(lib, K=0) == ARG
+    assert call(lib, K=129) == UNSUP
+    assert call(lib, d=66) == UNSUP
+    assert call(lib, dg=18) == UNSUP
+    assert call(lib, dg=2048) == ARG
+    assert call(lib, Hq=6, Hkv=4) == ARG
+    assert call(lib, Hq=6, Hkv=2) == UNSUP
+    assert call(lib, dh=96) == UNSUP
+    assert call(lib, n=1 << 26, Hq=64, Hkv=8) == SHAPE
+    for name in ("h", "w", "c", "q", "k", "v"):
+        assert call(lib, **{name: None}) == ARG, name
+    assert call(lib, k=MIS) == ALIGN
+    assert call(lib, ws=None) == WS
+    assert call(lib, wsb=64) == WS
+    assert call(lib, out=None) == ARG
+
+
+def test_soft_train_backward_outputs(lib):
+    assert _train_bwd(lib, dc=None) == ARG
+    assert _train_bwd(lib, dw=None) == ARG
+    assert _train_bwd(lib, dout=None) == ARG
+    assert _train_bwd(lib, lse=None) == ARG
+    assert _train_bwd(lib, dc=P + 2) == ALIGN
+    assert _train_bwd(lib, dout=MIS) == ALIGN
+    f = lib.focus_soft_train_workspace_size
+    assert f(-1, 64, 16, 8, 8, 2) == 0
+    # the scores, the soft assignment's planes and the backward's per-token buffers at least
+    assert f(32768, 4096, 128, 64, 32, 3) >= 32768 * (64 * 4 * 3 + 64 * 2 * 2 + 32 * 4 + 128 * 8)

@@ -98,7 +98,22 @@ def slots_append_args(**over):
     return a
 
 
+def train_fwd_args(**over):
+    a = dict(hidden=f32(n, 16), w_g=f32(16, 8), centroids=f32(K, 8), sinkhorn_iters=2,
+             q=bf(n, Hq, dh), k=bf(n, Hkv, dh), v=bf(n, Hkv, dh), window=2, lam=3.0)
+    a.update(over)
+    return a
+
+
+def train_bwd_args(**over):
+    a = train_fwd_args()
+    a.update(out=bf(n, Hq, dh), lse=f32(n, Hq), dout=bf(n, Hq, dh))
+    a.update(over)
+    return a
+
+
 WRAPPERS = {
+    "focus_soft_train_forward": train_fwd_args, "focus_soft_train_backward": train_bwd_args,
     "focus_assign": assign_args, "focus_bucket": lambda **o: {"groups": i32(n, k), "K": K, **o},
     "focus_attention": attn_args, "focus_attention_asym": asym_args,
     "focus_soft_attention": soft_args, "focus_bucket_append": append_args,
@@ -162,6 +177,14 @@ MISMATCHES = [
     ("focus_slots_append", dict(seg_len=i32(B, K + 1)), "seg_len"),
     ("focus_slots_append", dict(cache_len=i32(B + 2)), "cache_len"),
     ("focus_slots_append", dict(overflow=i32(2)), "overflow"),
+    ("focus_soft_train_forward", dict(q=bf(n + 1, Hq, dh)), "k"),
+    ("focus_soft_train_forward", dict(hidden=f32(n + 1, 16)), "tokens"),
+    ("focus_soft_train_forward", dict(centroids=f32(K, 9)), "centroids"),
+    ("focus_soft_train_forward", dict(lse=f32(n, Hq + 1)), "lse"),
+    ("focus_soft_train_backward", dict(dout=bf(n, Hq, dh + 8)), "dout"),
+    ("focus_soft_train_backward", dict(lse=f32(n - 1, Hq)), "lse"),
+    ("focus_soft_train_backward", dict(d_w_g=f32(15, 8)), "d_w_g"),
+    ("focus_soft_train_backward", dict(d_hidden=f32(n, 17)), "d_hidden"),
 ]
 
 

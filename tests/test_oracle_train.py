@@ -124,3 +124,14 @@ def test_soft_assignment_is_the_balanced_plan():
     gd = load_golden("balanced_rank_n3.json")
     g = soft_assignment_ref(*(np.array(gd[x]) for x in ("hidden", "w_g", "centroids")), gd["iters"])
     np.testing.assert_allclose(g, np.array(gd["plan"]), atol=1e-12)
+
+
+def test_sampled_rows_equal_the_full_forward():
+    from oracle.train_ref import soft_train_forward_rows_ref
+    p = _problem(30, 6, 4, 3, 4, 2, 5, seed=21)
+    out, lse, g = soft_train_forward_ref(p["hidden"], p["w_g"], p["centroids"], 2, p["q"], p["k"],
+                                         p["v"], 3, 5.0)
+    rows = np.array([0, 1, 7, 29])
+    o_r, l_r = soft_train_forward_rows_ref(g, p["q"], p["k"], p["v"], 3, 5.0, rows)
+    np.testing.assert_allclose(o_r, out[rows], atol=1e-12)
+    np.testing.assert_allclose(l_r, lse[rows], atol=1e-12)
