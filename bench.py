@@ -34,7 +34,9 @@ from learned_centroid_gated_amd import (focus_assign, focus_assign_workspace_siz
                                         focus_bucket_workspace_size, focus_decode,
                                         focus_decode_paged, focus_decode_slots,
                                         focus_slots_append, focus_slots_from_bucket,
-                                        focus_soft_attention)
+                                        focus_soft_attention, focus_soft_train_backward,
+                                        focus_soft_train_forward,
+                                        focus_soft_train_workspace_size)
 from learned_centroid_gated_amd import _lib  # noqa: E402
 from synth import CONFIGS, assign_inputs, qkv_inputs, random_groups  # noqa: E402
 
@@ -413,6 +415,63 @@ def asym_bench(c, st, dense_ms, sym_attn_ms, reps=3):
     return res
 
 
+# ------------------------------------------------------------------ training
+def train_bench(c, lam=10.0, reps=3):
+    """One soft-gated training step on the workload's shapes: the forward over every causal pair
+    (gate from the soft assignment) and the backward to the centroids and the projection, with an
+    N(0,1) bf16 upstream gradient. Algorithmic flop: forward 4 dh Hq per causal pair; backward
+    4 dh Hq per far pair (the logits and dP once; the kernels recompute them on both sides)."""
+    log(f"[bench] training step {c.name}: n={c.n} lambda={lam}")
+    a = assign_inputs(c.n, c.d, c.dg, c.K, c.mix, c.weights, c.noise_frac, index=c.index,
+                      device="cuda")
+    t = qkv_inputs(c.n, c.Hq, c.Hkv, c.dh, index=c.index, device="cuda")
+    dout = qkv_inputs(c.n, c.Hq, c.Hkv, c.dh, index=c.index, salt=31, device="cuda", which="q")["q"]
+    dev = t["q"].device
+    ws = torch.empty(focus_soft_train_workspace_size(c.n, c.d, c.dg, c.K, c.Hq, c.iters),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((c.n, c.Hq, c.dh), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((c.n, c.Hq), dtype=torch.float32, device=dev)
+    dc = torch.empty((c.K, c.dg), dtype=torch.float32, device=dev)
+    dw = torch.empty((c.d, c.dg), dtype=torch.float32, device=dev)
+    args = (a["hidden"], a["w_g"], a["centroids"], c.iters, t["q"], t["k"], t["v"])
+
+    def fwd():
+        focus_soft_train_forward(*args, c.window, lam, out=out, lse=lse, workspace=ws)
+
+    def bwd():
+        focus_soft_train_backward(*args, out, lse, dout, c.window, lam, d_centroids=dc,
+                                  d_w_g=dw, workspace=ws)
+
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms, b_ms = [], []
+    for _ in range(reps):
+        ev[0].record()
+        fwd()
+        ev[1].record()
+        bwd()
+        ev[2].record()
+        torch.cuda.synchronize()
+        f_ms.append(ev[0].elapsed_time(ev[1]))
+        b_ms.append(ev[1].elapsed_time(ev[2]))
+    n, w = c.n, min(c.window, c.n)
+    causal = n * (n + 1) / 2
+    far = (n - w) * (n - w + 1) / 2 if n > w else 0.0  # pairs with i - j >= window
+    fl = 4.0 * c.dh * c.Hq
+    fm, bm = float(np.median(f_ms)), float(np.median(b_ms))
+    res = {"workload": c.name, "lambda": lam, "forward_ms": fm, "backward_ms": bm,
+           "step_ms": fm + bm, "tokens_per_s": n / ((fm + bm) * 1e-3),
+           "forward_tflops": fl * causal / (fm * 1e-3) / 1e12,
+           "backward_tflops_algorithmic": fl * far / (bm * 1e-3) / 1e12,
+           "grad_norms": {"d_centroids": float(dc.norm()), "d_w_g": float(dw.norm())}}
+    log(f"[bench]   training {c.name}: forward {fm:.3f} ms ({res['forward_tflops']:.0f} TF), "
+        f"backward {bm:.3f} ms ({res['backward_tflops_algorithmic']:.0f} TF algorithmic)")
+    del a, t, dout, ws
+    return res
+
+
 # ------------------------------------------------------------------ decode
 def decode_bench(c, steps, warmup):
     log(f"[bench] decode {c.name}: B={c.batch} L={c.n} Hq={c.Hq}/{c.Hkv} K={c.K} top_k={c.top_k} "
@@ -686,6 +745,9 @@ def main():
             del st
             torch.cuda.empty_cache()
         extra["decode_b64_l64k"] = decode_bench(cfg["decode_b64_l64k"], 20, 3)
+        torch.cuda.empty_cache()
+        extra["training_step"] = {name: train_bench(cfg[name]) for name in ("gpt2s_n2k",
+                                                                             "gqa7b_n32k")}
         torch.cuda.empty_cache()
     line = {
         "metric": METRIC, "value": res3["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
