@@ -690,6 +690,8 @@ def main():
                     help="only the batched decode workload (prints its own JSON line)")
     ap.add_argument("--workload", default=None,
                     help="time one prefill workload only, e.g. long_n1m (prints its own JSON line)")
+    ap.add_argument("--train", default=None,
+                    help="time the soft-gated training step of one workload only, e.g. gqa7b_n32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB copy, to scale HBM byte counters")
@@ -708,6 +710,9 @@ def main():
     if args.calibrate_copy:
         calibration_copy()
     cfg = {x.name: x for x in CONFIGS}
+    if args.train:
+        print(json.dumps(train_bench(cfg[args.train])), flush=True)
+        return
     if args.workload:
         res, st = prefill_bench(cfg[args.workload], args.steps, args.warmup, hip)
         res.pop("_groups")
