@@ -160,6 +160,9 @@ int focus_bucket_append(const int32_t* new_groups, const int32_t* cache_len, int
  *   out      device, out [n, Hq, d_head] bf16.
  *   lse      device, out [n, Hq] fp32.
  *   workspace  at least focus_attention_workspace_size(n, Hq, Hkv, d_head, K, top_k) bytes.
+ * Range: the group parts are kept in fp16 between the two passes. Each is a softmax-weighted
+ * average of v rows, so its entries are bounded by max |v|; v entries must stay below 65504 in
+ * magnitude (the largest fp16 value), else the merged output overflows.
  * ------------------------------------------------------------------------------------ */
 size_t focus_attention_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K, int top_k);
 int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -204,7 +207,7 @@ int focus_attention_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   top_k    1 <= top_k <= min(K, 4), groups each query looks at.
  *   k_offsets, k_idx, k_slot   device, focus_bucket output for k_group [n, 1] (batch 1).
  *   workspace  at least focus_attention_asym_workspace_size(n, Hq, Hkv, d_head, K, top_k)
- *            bytes. Errors as for focus_attention; asynchronous on `stream`.
+ *            bytes. Errors and the range of v as for focus_attention; asynchronous on `stream`.
  * ------------------------------------------------------------------------------------ */
 size_t focus_attention_asym_workspace_size(int64_t n, int Hq, int Hkv, int d_head, int K,
                                            int top_k);

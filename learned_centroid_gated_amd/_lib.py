@@ -5,7 +5,9 @@ Loading fails loudly when the library has not been built; there is no fallback p
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfocus.so")
+# FOCUS_LIB_PATH selects another build of the same library (the host-sanitized one in tests)
+LIB_PATH = os.environ.get("FOCUS_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfocus.so")
 
 c_i64, c_int, c_sz, c_f, c_p = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 

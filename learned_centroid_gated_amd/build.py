@@ -65,6 +65,46 @@ def build(jobs=None, verbose=False):
     return LIB
 
 
+# Host-sanitized variant of the library for checking the C-ABI layer on a machine without a GPU:
+# focus_api.hip (argument validation, workspace carving, launch order) is compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer on its host code only; the kernels' objects are
+# the normal build's. Load it with the sanitizer runtime preloaded (sanitizer_runtime()).
+SAN_LIB = os.path.join(BUILD, "libfocus_san.so")
+SAN_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+
+
+def sanitizer_runtime():
+    """Path of the AddressSanitizer runtime that a plain interpreter must preload."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime was not found next to hipcc")
+    return path
+
+
+def build_sanitized(verbose=False):
+    """Compile focus_api.hip with host-side ASan and UBSan and link it with the other objects
+    of the normal build (built first if missing). Returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in SOURCES[1:]:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj if os.path.exists(obj) else _compile(src, verbose))
+    san_obj = os.path.join(BUILD, "focus_api_san.o")
+    cflags = [f for f in CFLAGS if f != "-O3"] + ["-O1", "-g"]
+    cmd = [hipcc(), *cflags, *SAN_FLAGS, "-Xarch_host", "-fno-omit-frame-pointer", "-c",
+           os.path.join(CSRC, "focus_api.hip"), "-o", san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized build of focus_api.hip failed:\n{r.stdout}{r.stderr}")
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, san_obj,
+                        *objs, "-o", SAN_LIB], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
