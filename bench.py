@@ -266,7 +266,7 @@ def prefill_bench(c, steps, warmup, hip, capture=False):
     res["gather_GBs"] = gather_bytes / (stage_ms["gather"] * 1e-3) / 1e9
     fold = c.d * c.K <= c.d * c.dg + c.dg * c.K
     assign_flops = 2.0 * c.n * c.d * c.K if fold else 2.0 * c.n * (c.d * c.dg + c.dg * c.K)
-    # fp32 score products per second (run as six bf16 part products each on the matrix cores)
+    # fp32 score products per second (run as three fp16 part products each on the matrix cores)
     res["assign_score_tflops"] = assign_flops / (assign_ms * 1e-3) / 1e12
     res["assign_hidden_GBs"] = c.n * c.d * 4 / (assign_ms * 1e-3) / 1e9
     # the dominant kernel of the step

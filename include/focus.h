@@ -65,6 +65,9 @@ int focus_version(void);
  * focus_assign - centroid group assignment (ZH 2.1.1 and 2.1.3; NL Kerncomponenten 1, 2, 4).
  *
  *   S = (hidden * w_g) * centroids^T                     scores, [n, K], fp32 arithmetic
+ *       (products at fp32-level accuracy: fp32 operands split exactly into two fp16 parts,
+ *       three part products on the matrix cores; a row holding a hidden value beyond fp16's
+ *       largest finite value, 65504, has its scores recomputed with fp32 FMAs)
  *   repeat sinkhorn_iters times (log domain, unit temperature, u = v = 0 at the start):
  *     u_i = -logsumexp_c (S_ic + v_c)                    every token carries mass 1
  *     v_c = log(n / K) - logsumexp_i (S_ic + u_i)        every group receives mass n / K

@@ -1,6 +1,6 @@
-// Centroid group assignment on gfx950: scores S = (H W_g) C^T on the bf16 matrix cores (fp32
-// operands split exactly into three bf16 parts), log-domain Sinkhorn balancing and top-k
-// membership.
+// Centroid group assignment on gfx950: scores S = (H W_g) C^T on the matrix cores (fp32
+// operands split exactly into two fp16 parts, or three bf16 parts), log-domain Sinkhorn
+// balancing and top-k membership.
 //
 // Method: "Why Attend to Everything? Focus is the Key" (Chinese technical summary,
 // gist.science/zh, section 2.1.1: projection into centroid space, similarity to K centroids,
@@ -17,10 +17,11 @@ namespace focus {
 //
 // Each fp32 operand x is split into three bf16 parts x = h + m + l + r: h = bf16(x),
 // m = bf16(x - h), l = bf16(x - h - m), rounding to nearest even, with both subtractions exact
-// in fp32. Then |m| <= 2^-9 |x|, |l| <= 2^-18 |x| and |r| <= 2^-27 |x|. A product a b keeps the
-// six part products hh, hm, mh, hl, mm, lh; the dropped ones (ml, lm, ll) and the residues add
-// up to less than about 2^-25 |a b|, so each product carries fp32-level relative error. The
-// six 32x32x16 bf16 MFMAs take 192 cycles where the fp32 MFMA needs 512 for the same block.
+// in fp32. bf16 keeps 8 significant bits, so |m| <= 2^-8 |x|, |l| <= 2^-16 |x| and
+// |r| <= 2^-24 |x|. A product a b keeps the six part products hh, hm, mh, hl, mm, lh; the
+// dropped ones (ml, lm, ll) and the residues add up to less than about 2^-22 |a b|, i.e.
+// fp32-level relative error. The six 32x32x16 bf16 MFMAs take 192 cycles where the fp32 MFMA
+// needs 512 for the same block.
 //
 // Block tile 128 x (32*NT), k-chunks of 32: the chunk's fp32 tiles come from global memory into
 // registers one chunk ahead, are split, and are stored as three bf16 planes per operand in
@@ -325,6 +326,323 @@ hipError_t launch_gemm_nt_f32_planes(const float* A, const __bf16* Bp, float* C,
     hipLaunchKernelGGL(gemm_nt_planes_kernel<4>, dim3(mb, (N + 127) / 128), block, 0, stream, A,
                        Bp, C, M, N, Kd, ldc);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- fp16 pair GEMM
+// The same product from two-part fp16 splits on the fp16 matrix cores: x = h + m + r with
+// h = fp16(x), m = fp16(x - h) (the subtraction is exact in fp32), rounding to nearest even.
+// fp16 keeps 11 significant bits, so |m| <= 2^-11 |x| and |r| <= 2^-22 |x| while x - h is in
+// fp16's normal range; below it (|x| < 2^-3) r is at most 2^-25 in absolute value. A product
+// keeps hh, hm and mh; the dropped mm and the residues leave less than about 3 * 2^-22 of
+// sum_k |a_k b_k| per output (plus 2^-25 sum_k |b_k| for A's small elements): fp32-level
+// accuracy from three part products where the bf16 split needs six.
+//
+// fp16's range: each row n of B is scaled by an exact power of two 2^e_n that puts its largest
+// magnitude in [2^14, 2^15) before splitting (split_pairs_kernel), and the output column is
+// multiplied back by 2^-e_n. A is split as it is, so an element of magnitude above fp16's
+// largest finite value (65504) or a non-finite one makes its row's outputs non-finite: such
+// rows are appended to a list (flag_list, counted by flag_count) for an exact recomputation.
+//
+// Block tile (32 WAVES) x (32 NT), k-chunks of 32 as in the bf16 kernels: A streams from global
+// memory into registers one chunk ahead and is split into two fp16 planes in LDS; B's planes
+// were split once per call and go from memory straight into a double buffer in LDS.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+struct F16x4Pair {
+  f16x4_t h, m;
+};
+__device__ __forceinline__ F16x4Pair split_pair(f32x4_t x) {
+  F16x4Pair p;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 h = (_Float16)x[e];
+    p.h[e] = h;
+    p.m[e] = (_Float16)(x[e] - (float)h);
+  }
+  return p;
+}
+
+// P[0][n][k] = h and P[1][n][k] = m of B[n][k] 2^e_n; scale_inv[n] = 2^-e_n. One block per row.
+__global__ __launch_bounds__(256) void split_pairs_kernel(const float* __restrict__ B, int Kd,
+                                                          int64_t count, _Float16* __restrict__ P,
+                                                          float* __restrict__ scale_inv) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * Kd;
+  float mx = 0.f;
+  for (int k = tid; k < Kd; k += 256) mx = fmaxf(mx, fabsf(B[base + k]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (l == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (mx > 0.f && mx <= 3.402823466e38f) {
+    int E;
+    frexpf(mx, &E);  // mx in [2^(E-1), 2^E)
+    e = 15 - E;
+  }
+  if (tid == 0) scale_inv[blockIdx.x] = ldexpf(1.f, -e);
+  for (int k = tid; k < Kd; k += 256) {
+    const float y = ldexpf(B[base + k], e);
+    const _Float16 h = (_Float16)y;
+    P[base + k] = h;
+    P[count + base + k] = (_Float16)(y - (float)h);
+  }
+}
+
+template <int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 4) void gemm_nt_f16x3_kernel(
+    const float* __restrict__ A, const _Float16* __restrict__ Bp,
+    const float* __restrict__ bscale, float* __restrict__ C, int64_t M, int N, int Kd, int ldc,
+    int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count) {
+  constexpr int NTH = 64 * WAVES;
+  constexpr int BM = 32 * WAVES, BN = 32 * NT, BK = 32;
+  constexpr int BTILE = 2 * BN * BK;           // fp16 per B tile (two planes)
+  constexpr int BINSTS = BTILE * 2 / 1024;     // 1 KB copies per B tile
+  constexpr int BPW = (BINSTS + WAVES - 1) / WAVES;
+  constexpr int AV = BM * BK / 4 / NTH;        // float4 of A per thread per chunk
+  static_assert(AV * 4 * NTH == BM * BK, "A tile splits evenly over the threads");
+  __shared__ __attribute__((aligned(1024))) _Float16 As[2][BM * BK];
+  __shared__ __attribute__((aligned(1024))) _Float16 Bs[2][BTILE];
+  const int tid = threadIdx.x, l = tid & 63, j = l & 31, g = l >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+
+  // copy ii of a B tile fills rows 16 (ii % (BN / 16)) .. + 15 of plane ii / (BN / 16), with the
+  // quarter permutation of plane_at (rows past N re-read row N - 1; their columns are not stored)
+  uint32_t boff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int ii = wave + WAVES * i;
+    const int pl = ii / (BN / 16), rb = ii % (BN / 16);
+    const int r = rb * 16 + l / 4;
+    const int q = (l % 4) ^ ((r >> 2) & 3);
+    const int row = min(n0 + r, N - 1);
+    boff[i] = (uint32_t)((((int64_t)pl * N + row) * Kd + 8 * q) * 2);
+  }
+  auto copy_b = [&](int k0, _Float16* dst) __attribute__((always_inline)) {
+    const char* base = (const char*)(Bp + k0);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int ii = wave + WAVES * i;
+      if (ii < BINSTS) dma16(base, boff[i], (char*)dst + ii * 1024);
+    }
+  };
+  auto lds_barrier = []() __attribute__((always_inline)) {  // LDS only: copies stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16_t{};
+
+  f32x4_t ra[AV];
+  auto load_a = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int e = tid + NTH * i, r = e >> 3, c = (e & 7) * 4;
+      const int64_t gr = m0 + r;
+      ra[i] = gr < M ? *(const f32x4_t*)(A + gr * Kd + k0 + c) : f32x4_t{};
+    }
+  };
+
+  auto chunk = [&](int k0, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;  // B buffer of this chunk
+    lds_barrier();  // every wave is done with As and with the other B buffer
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int e = tid + NTH * i, r = e >> 3, c = (e & 7) * 4;
+      const F16x4Pair pr = split_pair(ra[i]);
+      const int o = plane_at(r, c);
+      *(f16x4_t*)&As[0][o] = pr.h;
+      *(f16x4_t*)&As[1][o] = pr.m;
+    }
+    // the wait for ra (the newest loads) also covers this chunk's B copies, issued before them
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (k0 + BK < Kd) {
+      copy_b(k0 + BK, Bs[P ^ 1]);
+      load_a(k0 + BK);
+    }
+    lds_barrier();  // As and this chunk's B planes are in LDS
+    const _Float16* bsb = Bs[P];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      f16x8_t a[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        a[p] = *(const f16x8_t*)&As[p][plane_at(wave * 32 + j, ks * 16 + 8 * g)];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f16x8_t b[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          b[p] = *(const f16x8_t*)&bsb[p * BN * BK + plane_at(t * 32 + j, ks * 16 + 8 * g)];
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1], b[0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], b[1], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], b[0], acc[t], 0, 0, 0);
+      }
+    }
+  };
+  copy_b(0, Bs[0]);
+  load_a(0);
+  for (int k0 = 0; k0 < Kd; k0 += 2 * BK) {
+    chunk(k0, std::integral_constant<int, 0>{});
+    if (k0 + BK < Kd) chunk(k0 + BK, std::integral_constant<int, 1>{});
+  }
+
+  // accumulator element v of tile t is row wave*32 + (v/4)*8 + 4g + v%4, column t*32 + j
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = n0 + t * 32 + j;
+    const float sc = col < N ? bscale[col] : 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + wave * 32 + (v >> 2) * 8 + 4 * g + (v & 3);
+      if (row < M && col < N) C[row * ldc + col] = acc[t][v] * sc;
+    }
+  }
+  // a row with a non-finite output had an element of A outside fp16's range (or not finite):
+  // every column of that row is then non-finite, so the first column block lists it
+  if (flag_list && blockIdx.y == 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      bool bad = false;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) bad = bad || !__builtin_isfinite(acc[t][v]);
+      const uint64_t bal = __ballot(bad);
+      if (l == 0 && bal != 0) {
+        const int64_t r0 = m0 + wave * 32 + (v >> 2) * 8 + (v & 3);
+        if ((uint32_t)bal != 0u && r0 < M) flag_list[atomicAdd(flag_count, 1)] = (int32_t)r0;
+        if ((uint32_t)(bal >> 32) != 0u && r0 + 4 < M)
+          flag_list[atomicAdd(flag_count, 1)] = (int32_t)(r0 + 4);
+      }
+    }
+  }
+}
+
+template <int NT, int WAVES>
+static int f16x3_blocks_per_cu() {  // resident blocks per CU, from the compiled resources
+  static int v = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, gemm_nt_f16x3_kernel<NT, WAVES>,
+                                                     64 * WAVES, 0) != hipSuccess)
+      b = 1;
+    return b > 0 ? b : 1;
+  }();
+  return v;
+}
+
+template <int NT>
+static void f16x3_launch(const float* A, const _Float16* Bp, const float* bscale, float* C,
+                         int64_t M, int N, int Kd, int ldc, int32_t* flags, int32_t* nflags,
+                         int cus, hipStream_t stream) {
+  // the HBM-bound time goes as rounds of resident blocks times the rows one round moves per CU:
+  // 256-row tiles unless 128-row ones finish in fewer such rows
+  const int b8 = f16x3_blocks_per_cu<NT, 8>(), b4 = f16x3_blocks_per_cu<NT, 4>();
+  const int64_t t8 = (M + 255) / 256, t4 = (M + 127) / 128;
+  const int64_t r8 = (t8 + (int64_t)cus * b8 - 1) / ((int64_t)cus * b8);
+  const int64_t r4 = (t4 + (int64_t)cus * b4 - 1) / ((int64_t)cus * b4);
+  const dim3 grid8(t8, (N + 32 * NT - 1) / (32 * NT)), grid4(t4, grid8.y);
+  if (r8 * b8 * 256 <= r4 * b4 * 128)
+    hipLaunchKernelGGL((gemm_nt_f16x3_kernel<NT, 8>), grid8, dim3(512), 0, stream, A, Bp, bscale,
+                       C, M, N, Kd, ldc, flags, nflags);
+  else
+    hipLaunchKernelGGL((gemm_nt_f16x3_kernel<NT, 4>), grid4, dim3(256), 0, stream, A, Bp, bscale,
+                       C, M, N, Kd, ldc, flags, nflags);
+}
+
+hipError_t launch_gemm_nt_f16x3(const float* A, const float* B, _Float16* Bp, float* bscale,
+                                float* C, int64_t M, int N, int Kd, int ldc, int32_t* flags,
+                                int32_t* nflags, hipStream_t stream) {
+  if (Kd % 32 != 0 || N < 1) return hipErrorInvalidValue;
+  if (M < 1) return hipSuccess;
+  hipLaunchKernelGGL(split_pairs_kernel, dim3(N), dim3(256), 0, stream, B, Kd, (int64_t)N * Kd,
+                     Bp, bscale);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (N <= 32) f16x3_launch<1>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, cus, stream);
+  else if (N <= 64) f16x3_launch<2>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, cus, stream);
+  else f16x3_launch<4>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, cus, stream);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- exact rows
+// Scores of the listed rows again in fp32, written over S: S[row, c] = h_row . Ft[c] (Ft [K, d],
+// row c the folded column W_g C_c^T), or (h_row W_g) . C[c] with W_g [d, d_g] and C [K, d_g].
+// For rows the fp16 product could not represent; one block per listed row at a time.
+__global__ __launch_bounds__(256) void exact_rows_kernel(
+    const float* __restrict__ H, int d, const float* __restrict__ Ft, const float* __restrict__ W,
+    const float* __restrict__ Cm, int dg, int K, const int32_t* __restrict__ list,
+    const int32_t* __restrict__ count, float* __restrict__ S, int ldS) {
+  __shared__ float part[4][1024];  // d_g <= 1024
+  __shared__ float zs[1024];
+  const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+  const int cnt = *count;
+  auto wave_sum = [](float s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    return s;
+  };
+  for (int li = blockIdx.x; li < cnt; li += gridDim.x) {
+    const int64_t row = list[li];
+    const float* h = H + row * d;
+    float* srow = S + row * ldS;
+    if (Ft) {
+      for (int c = wave; c < K; c += 4) {  // a wave per column, lanes over d (d % 4 == 0)
+        const float* f = Ft + (int64_t)c * d;
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 4 * l; k < d; k += 256) {
+          const f32x4_t hv = *(const f32x4_t*)(h + k), fv = *(const f32x4_t*)(f + k);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(hv[e], fv[e], a[e]);
+        }
+        const float s = wave_sum((a[0] + a[1]) + (a[2] + a[3]));
+        if (l == 0) srow[c] = s;
+      }
+    } else {
+      float z[16];  // columns l + 64 q of z = h W_g, over this wave's rows k = wave + 4 i
+#pragma unroll
+      for (int q = 0; q < 16; ++q) z[q] = 0.f;
+      for (int k = wave; k < d; k += 4) {
+        const float hk = h[k];
+        const float* wr = W + (int64_t)k * dg;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (l + 64 * q < dg) z[q] = __builtin_fmaf(hk, wr[l + 64 * q], z[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (l + 64 * q < dg) part[wave][l + 64 * q] = z[q];
+      __syncthreads();
+      for (int c = tid; c < dg; c += 256) zs[c] = (part[0][c] + part[1][c]) + (part[2][c] + part[3][c]);
+      __syncthreads();
+      for (int c = wave; c < K; c += 4) {  // a wave per centroid, lanes over d_g
+        const float* cr = Cm + (int64_t)c * dg;
+        float s = 0.f;
+        for (int k = l; k < dg; k += 64) s = __builtin_fmaf(zs[k], cr[k], s);
+        s = wave_sum(s);
+        if (l == 0) srow[c] = s;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_exact_rows(const float* H, int d, const float* Ft, const float* W,
+                             const float* Cm, int dg, int K, const int32_t* list,
+                             const int32_t* count, int64_t n, float* S, int ldS,
+                             hipStream_t stream) {
+  const int64_t blocks = n < 256 ? n : 256;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(exact_rows_kernel, dim3(blocks), dim3(256), 0, stream, H, d, Ft, W, Cm, dg,
+                     K, list, count, S, ldS);
   return hipGetLastError();
 }
 

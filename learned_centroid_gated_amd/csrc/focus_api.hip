@@ -49,9 +49,12 @@ struct AssignWs {
   float* S;
   float* Z;
   float* Bt;
-  __bf16* Bp;  // bf16 planes of the current product's B operand (3 x its size)
+  _Float16* Bp;     // fp16 planes of the current product's B operand (2 x its size)
+  float* bscale;    // per-row scales of those planes
   float* v;
   float2* partials;
+  int32_t* flags;   // rows whose scores the fp16 products could not represent
+  int32_t* nflags;
 };
 
 size_t assign_carve(void* ws, int64_t n, int d, int d_g, int K, AssignWs* out) {
@@ -62,9 +65,12 @@ size_t assign_carve(void* ws, int64_t n, int d, int d_g, int K, AssignWs* out) {
   w.Z = fold ? nullptr : c.take<float>((size_t)n * d_g);
   w.Bt = c.take<float>((size_t)(fold ? K : d_g) * d);
   const size_t bmax = fold ? (size_t)K * d : std::max((size_t)d_g * d, (size_t)K * d_g);
-  w.Bp = c.take<__bf16>(3 * bmax);
+  w.Bp = c.take<_Float16>(2 * bmax);
+  w.bscale = c.take<float>((size_t)std::max(K, d_g));
   w.v = c.take<float>((size_t)padded_k(K));
   w.partials = c.take<float2>((size_t)sinkhorn_blocks(n, K) * K);
+  w.flags = c.take<int32_t>((size_t)std::max<int64_t>(n, 1));
+  w.nflags = c.take<int32_t>(1);
   if (out) *out = w;
   return c.used;
 }
@@ -246,25 +252,31 @@ int focus_assign(const float* hidden, const float* w_g, const float* centroids, 
   hipStream_t st = (hipStream_t)stream;
   const int ldS = padded_k(K);
   hipError_t e;
-  // the n-row products take their small operand as bf16 planes split once per call (needs the
-  // inner dimension to be a multiple of 32), else split on the fly
+  // The n-row products run as fp16 pair products (inner dimension a multiple of 32), else as
+  // the bf16 split product. Rows the fp16 products cannot represent (hidden values beyond
+  // fp16's range) are listed and their scores recomputed exactly before Sinkhorn.
+  bool listed = false;
   auto product = [&](const float* a, const float* b, float* c, int64_t m, int nn, int kd,
                      int ldc) -> hipError_t {
     if (kd % 32 != 0) return launch_gemm_nt_f32(a, b, c, m, nn, kd, ldc, st);
-    hipError_t e2 = launch_split_planes(b, (int64_t)nn * kd, w.Bp, st);
-    if (e2 != hipSuccess) return e2;
-    return launch_gemm_nt_f32_planes(a, w.Bp, c, m, nn, kd, ldc, st);
+    listed = true;
+    return launch_gemm_nt_f16x3(a, b, w.Bp, w.bscale, c, m, nn, kd, ldc, w.flags, w.nflags, st);
   };
-  if (assign_folds(d, d_g, K)) {
+  const bool fold = assign_folds(d, d_g, K);
+  e = launch_fill_i32(w.nflags, 0, 1, st);
+  if (e == hipSuccess && fold) {
     // Bt = (W_g C^T)^T = C W_g^T  [K, d];  S = H Bt^T
     e = launch_gemm_nt_f32(centroids, w_g, w.Bt, K, d, d_g, d, st);
     if (e == hipSuccess) e = product(hidden, w.Bt, w.S, n, K, d, ldS);
-  } else {
+  } else if (e == hipSuccess) {
     // Bt = W_g^T [d_g, d];  Z = H W_g;  S = Z C^T
     e = launch_transpose_f32(w_g, w.Bt, d, d_g, st);
     if (e == hipSuccess) e = product(hidden, w.Bt, w.Z, n, d_g, d, d_g);
     if (e == hipSuccess) e = product(w.Z, centroids, w.S, n, K, d_g, ldS);
   }
+  if (e == hipSuccess && listed)
+    e = launch_exact_rows(hidden, d, fold ? w.Bt : nullptr, w_g, centroids, d_g, K, w.flags,
+                          w.nflags, n, w.S, ldS, st);
   if (e == hipSuccess) e = launch_fill_f32(w.v, 0.f, K, st);
   const int nblk = sinkhorn_blocks(n, K);
   for (int t = 0; t < sinkhorn_iters && e == hipSuccess; ++t)

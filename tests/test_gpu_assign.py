@@ -66,6 +66,69 @@ def test_assign_matches_oracle(n, d, dg, K, top_k, iters, mix):
     _check_groups(g, ref, ref["S"] + ref["v"][None, :])
 
 
+CROWDED = [
+    # n, d, dg, K, top_k, iters, scaled   (fold; two products; K and d_g wider than a block; the
+    # bf16 split product for d % 32 != 0; small hidden states)
+    (4096, 512, 128, 64, 2, 3, "w_g"),
+    (4096, 256, 16, 64, 1, 2, "w_g"),
+    (2000, 128, 32, 1024, 8, 2, "w_g"),
+    (1500, 64, 512, 300, 3, 2, "w_g"),
+    (1000, 260, 8, 5, 3, 1, "w_g"),
+    (4096, 512, 128, 64, 2, 3, "hidden"),
+    (4096, 256, 16, 64, 1, 2, "hidden"),
+]
+
+
+@pytest.mark.parametrize("n,d,dg,K,top_k,iters,scaled", CROWDED)
+def test_assign_crowded_scores(n, d, dg, K, top_k, iters, scaled):
+    """One operand scaled by 1e-3 crowds the scores: most tokens' k-th and (k+1)-th balanced
+    scores lie within 1e-3 of each other, so score errors far below that would already show as
+    mismatches outside the tie window. Scaling the hidden states puts most of their elements
+    below fp16's normal range, where the library's fp16 split keeps an absolute error only."""
+    say(f"assign crowded n={n} d={d} dg={dg} K={K} top_k={top_k} iters={iters} ({scaled} x 1e-3)")
+    a = assign_inputs(n, d, dg, K, K, index=0, salt=3 * n + K)
+    h, w = a["hidden"], a["w_g"]
+    if scaled == "w_g":
+        w = w * np.float32(1e-3)
+    else:
+        h = h * np.float32(1e-3)
+    ref = assign_ref(h, w, a["centroids"], top_k, iters)
+    b = -np.sort(-(ref["S"] + ref["v"][None, :]), axis=1)
+    near = float((b[:, top_k - 1] - b[:, top_k] < 1e-3).mean())
+    say(f"  {near:.0%} of tokens within 1e-3 at the k-th place")
+    assert near > 0.5
+    g, v = _run(h, w, a["centroids"], top_k, iters)
+    np.testing.assert_allclose(v, ref["v"], rtol=0, atol=2e-5)
+    _check_groups(g, ref, ref["S"] + ref["v"][None, :])
+
+
+@pytest.mark.parametrize("n,d,dg,K,top_k,iters", [(3000, 512, 128, 64, 2, 3),
+                                                   (3000, 256, 32, 128, 1, 2)])
+def test_assign_hidden_beyond_fp16_range(n, d, dg, K, top_k, iters):
+    """Some tokens carry hidden values beyond fp16's largest finite value (65504) in three
+    channels whose rows of W_g are small (large activations on channels the projection
+    damps), so scores stay of order one; other tokens sit at fp16's edge in the same channels.
+    The library's fp16 score products cannot represent the former: it lists those tokens and
+    recomputes their scores exactly in fp32 before balancing (folded plan and two-product plan,
+    where both products list the token). Groups and potentials must still match the oracle."""
+    say(f"assign beyond fp16 range n={n} d={d} dg={dg} K={K}")
+    a = assign_inputs(n, d, dg, K, K, index=0, salt=7 * n + K)
+    h, w = a["hidden"].copy(), a["w_g"].copy()
+    w[:3] *= np.float32(1e-4)
+    rs = np.random.default_rng(n + d)
+    big = rs.choice(n, 40, replace=False)
+    for i, r in enumerate(big):
+        h[r, :1 + i % 3] = np.float32((1 if i % 2 else -1) * (7e4 + 3e4 * i))
+    edge = rs.choice(np.setdiff1d(np.arange(n), big), 20, replace=False)
+    h[edge, 0] = np.float32(65504.0)
+    h[edge[:10], 1] = np.float32(-65519.0)
+    ref = assign_ref(h, w, a["centroids"], top_k, iters)
+    assert np.abs(ref["S"]).max() < 50.0
+    g, v = _run(h, w, a["centroids"], top_k, iters)
+    np.testing.assert_allclose(v, ref["v"], rtol=0, atol=2e-5)
+    _check_groups(g, ref, ref["S"] + ref["v"][None, :])
+
+
 def test_assign_deterministic():
     a = assign_inputs(5000, 256, 64, 32, 32, index=0, salt=77)
     g1, v1 = _run(a["hidden"], a["w_g"], a["centroids"], 2, 3)
