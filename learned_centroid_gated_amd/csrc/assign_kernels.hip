@@ -329,6 +329,41 @@ hipError_t launch_gemm_nt_f32_planes(const float* A, const __bf16* Bp, float* C,
   return hipGetLastError();
 }
 
+// ============================================================================ row layouts
+// A row of K scores is spread over LPR lanes; lane q of the row holds columns
+// 4q + 4*LPR*c + e (c < CPL, e < 4). Rows per wave: 64 / LPR.
+// Row reductions over the row's LPR lanes (an aligned group): within a 16-lane row by VALU
+// lane moves (pairs, quads, half-row mirror, row mirror: each step combines two disjoint
+// halves of the group so far), across rows by lane shuffles.
+template <int LPR>
+__device__ __forceinline__ float row_max(float x) {
+  if constexpr (LPR >= 2) x = fmaxf(x, dpp_move<0xB1>(x));
+  if constexpr (LPR >= 4) x = fmaxf(x, dpp_move<0x4E>(x));
+  if constexpr (LPR >= 8) x = fmaxf(x, dpp_move<0x141>(x));
+  if constexpr (LPR >= 16) x = fmaxf(x, dpp_move<0x140>(x));
+  if constexpr (LPR >= 32) x = fmaxf(x, shfl_xor_f(x, 16));
+  if constexpr (LPR >= 64) x = fmaxf(x, shfl_xor_f(x, 32));
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (LPR >= 2) x += dpp_move<0xB1>(x);
+  if constexpr (LPR >= 4) x += dpp_move<0x4E>(x);
+  if constexpr (LPR >= 8) x += dpp_move<0x141>(x);
+  if constexpr (LPR >= 16) x += dpp_move<0x140>(x);
+  if constexpr (LPR >= 32) x += shfl_xor_f(x, 16);
+  if constexpr (LPR >= 64) x += shfl_xor_f(x, 32);
+  return x;
+}
+
+// Merge two (max, sum) summaries of exp: sum_i exp(x_i) = exp(m) * s.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * fast_exp2((m - M) * kLog2e) + s2 * fast_exp2((m2 - M) * kLog2e);
+  m = M;
+}
+
 // ---------------------------------------------------------------------------- fp16 pair GEMM
 // The same product from two-part fp16 splits on the fp16 matrix cores: x = h + m + r with
 // h = fp16(x), m = fp16(x - h) (the subtraction is exact in fp32), rounding to nearest even.
@@ -393,11 +428,17 @@ __global__ __launch_bounds__(256) void split_pairs_kernel(const float* __restric
   }
 }
 
+// With col_partials (the block then spans all N <= 32 NT columns): the epilogue also takes
+// Sinkhorn's first row step on the block's rows, u_r = -logsumexp_c C[r, c] (the column
+// potential starts at zero), and writes the block's summary of sum_r exp(C[r, c] + u_r) for
+// every column as a (max, sum) pair: col_partials[blockIdx.x * N + c]. Rows that are listed
+// (not finite) or past M stay out of the summary.
 template <int NT, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 4) void gemm_nt_f16x3_kernel(
+__global__ __launch_bounds__(64 * WAVES, NT > 4 ? 2 : 4) void gemm_nt_f16x3_kernel(
     const float* __restrict__ A, const _Float16* __restrict__ Bp,
     const float* __restrict__ bscale, float* __restrict__ C, int64_t M, int N, int Kd, int ldc,
-    int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count) {
+    int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count,
+    float2* __restrict__ col_partials) {
   constexpr int NTH = 64 * WAVES;
   constexpr int BM = 32 * WAVES, BN = 32 * NT, BK = 32;
   constexpr int BTILE = 2 * BN * BK;           // fp16 per B tile (two planes)
@@ -503,8 +544,9 @@ __global__ __launch_bounds__(64 * WAVES, 4) void gemm_nt_f16x3_kernel(
     const float sc = col < N ? bscale[col] : 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
+      acc[t][v] *= sc;
       const int64_t row = m0 + wave * 32 + (v >> 2) * 8 + 4 * g + (v & 3);
-      if (row < M && col < N) C[row * ldc + col] = acc[t][v] * sc;
+      if (row < M && col < N) C[row * ldc + col] = acc[t][v];
     }
   }
   // a row with a non-finite output had an element of A outside fp16's range (or not finite):
@@ -524,6 +566,56 @@ __global__ __launch_bounds__(64 * WAVES, 4) void gemm_nt_f16x3_kernel(
       }
     }
   }
+  if (col_partials) {
+    // row step: the 32 lanes of a half-wave hold one row's columns
+    float u[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + wave * 32 + (v >> 2) * 8 + 4 * g + (v & 3);
+      float mx = -INFINITY, bad = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t * 32 + j < N) {
+          mx = fmaxf(mx, acc[t][v]);
+          bad = __builtin_isfinite(acc[t][v]) ? bad : 1.f;
+        }
+      }
+      mx = row_max<32>(mx);
+      bad = row_max<32>(bad);
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t * 32 + j < N) sum += fast_exp2((acc[t][v] - mx) * kLog2e);
+      sum = row_sum<32>(sum);
+      u[v] = (row < M && bad == 0.f) ? -(mx + __logf(sum)) : -INFINITY;  // -inf: left out
+    }
+    // column summaries over the lane's 16 rows, then the other half-wave's, then the waves
+    lds_barrier();  // every wave is done reading B from LDS
+    float2* red = reinterpret_cast<float2*>(&Bs[0][0]);  // [WAVES][32 NT]
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float cm = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (u[v] != -INFINITY) cm = fmaxf(cm, acc[t][v] + u[v]);
+      float cs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (u[v] != -INFINITY) cs += fast_exp2((acc[t][v] + u[v] - cm) * kLog2e);
+      const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
+      const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs), __float_as_uint(cs), false, false);
+      float m = __uint_as_float(pm[0]), sm = __uint_as_float(ps[0]);
+      ms_merge(m, sm, __uint_as_float(pm[1]), __uint_as_float(ps[1]));
+      if (g == 0) red[wave * (32 * NT) + t * 32 + j] = make_float2(m, sm);
+    }
+    __syncthreads();
+    for (int c = tid; c < 32 * NT && c < N; c += 64 * WAVES) {
+      float m = red[c].x, sm = red[c].y;
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) ms_merge(m, sm, red[w * (32 * NT) + c].x, red[w * (32 * NT) + c].y);
+      col_partials[(int64_t)blockIdx.x * N + c] = make_float2(m, sm);
+    }
+  }
 }
 
 template <int NT, int WAVES>
@@ -539,37 +631,50 @@ static int f16x3_blocks_per_cu() {  // resident blocks per CU, from the compiled
 }
 
 template <int NT>
-static void f16x3_launch(const float* A, const _Float16* Bp, const float* bscale, float* C,
-                         int64_t M, int N, int Kd, int ldc, int32_t* flags, int32_t* nflags,
-                         int cus, hipStream_t stream) {
-  // the HBM-bound time goes as rounds of resident blocks times the rows one round moves per CU:
-  // 256-row tiles unless 128-row ones finish in fewer such rows
-  const int b8 = f16x3_blocks_per_cu<NT, 8>(), b4 = f16x3_blocks_per_cu<NT, 4>();
-  const int64_t t8 = (M + 255) / 256, t4 = (M + 127) / 128;
-  const int64_t r8 = (t8 + (int64_t)cus * b8 - 1) / ((int64_t)cus * b8);
-  const int64_t r4 = (t4 + (int64_t)cus * b4 - 1) / ((int64_t)cus * b4);
-  const dim3 grid8(t8, (N + 32 * NT - 1) / (32 * NT)), grid4(t4, grid8.y);
-  if (r8 * b8 * 256 <= r4 * b4 * 128)
-    hipLaunchKernelGGL((gemm_nt_f16x3_kernel<NT, 8>), grid8, dim3(512), 0, stream, A, Bp, bscale,
-                       C, M, N, Kd, ldc, flags, nflags);
-  else
-    hipLaunchKernelGGL((gemm_nt_f16x3_kernel<NT, 4>), grid4, dim3(256), 0, stream, A, Bp, bscale,
-                       C, M, N, Kd, ldc, flags, nflags);
+static int64_t f16x3_launch(const float* A, const _Float16* Bp, const float* bscale, float* C,
+                            int64_t M, int N, int Kd, int ldc, int32_t* flags, int32_t* nflags,
+                            float2* partials, int cus, hipStream_t stream) {
+  const int64_t t4 = (M + 127) / 128, t8 = (M + 255) / 256;
+  const int ny = (N + 32 * NT - 1) / (32 * NT);
+  if constexpr (NT == 8) {  // 256 columns: 128-row tiles only (two waves per SIMD)
+    hipLaunchKernelGGL((gemm_nt_f16x3_kernel<8, 4>), dim3(t4, ny), dim3(256), 0, stream, A, Bp,
+                       bscale, C, M, N, Kd, ldc, flags, nflags, partials);
+    return t4;
+  } else {
+    // the HBM-bound time goes as rounds of resident blocks times the rows one round moves per
+    // CU: 256-row tiles unless 128-row ones finish in fewer such rows
+    const int b8 = f16x3_blocks_per_cu<NT, 8>(), b4 = f16x3_blocks_per_cu<NT, 4>();
+    const int64_t r8 = (t8 + (int64_t)cus * b8 - 1) / ((int64_t)cus * b8);
+    const int64_t r4 = (t4 + (int64_t)cus * b4 - 1) / ((int64_t)cus * b4);
+    if (r8 * b8 * 256 <= r4 * b4 * 128) {
+      hipLaunchKernelGGL((gemm_nt_f16x3_kernel<NT, 8>), dim3(t8, ny), dim3(512), 0, stream, A, Bp,
+                         bscale, C, M, N, Kd, ldc, flags, nflags, partials);
+      return t8;
+    }
+    hipLaunchKernelGGL((gemm_nt_f16x3_kernel<NT, 4>), dim3(t4, ny), dim3(256), 0, stream, A, Bp,
+                       bscale, C, M, N, Kd, ldc, flags, nflags, partials);
+    return t4;
+  }
 }
 
 hipError_t launch_gemm_nt_f16x3(const float* A, const float* B, _Float16* Bp, float* bscale,
                                 float* C, int64_t M, int N, int Kd, int ldc, int32_t* flags,
-                                int32_t* nflags, hipStream_t stream) {
-  if (Kd % 32 != 0 || N < 1) return hipErrorInvalidValue;
+                                int32_t* nflags, float2* col_partials, int64_t* row_blocks,
+                                hipStream_t stream) {
+  if (Kd % 32 != 0 || N < 1 || (col_partials && N > 256)) return hipErrorInvalidValue;
+  if (row_blocks) *row_blocks = 0;
   if (M < 1) return hipSuccess;
   hipLaunchKernelGGL(split_pairs_kernel, dim3(N), dim3(256), 0, stream, B, Kd, (int64_t)N * Kd,
                      Bp, bscale);
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (N <= 32) f16x3_launch<1>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, cus, stream);
-  else if (N <= 64) f16x3_launch<2>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, cus, stream);
-  else f16x3_launch<4>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, cus, stream);
+  int64_t rb;
+  if (N <= 32) rb = f16x3_launch<1>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, col_partials, cus, stream);
+  else if (N <= 64) rb = f16x3_launch<2>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, col_partials, cus, stream);
+  else if (N <= 128 || !col_partials) rb = f16x3_launch<4>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, col_partials, cus, stream);
+  else rb = f16x3_launch<8>(A, Bp, bscale, C, M, N, Kd, ldc, flags, nflags, col_partials, cus, stream);
+  if (row_blocks) *row_blocks = rb;
   return hipGetLastError();
 }
 
@@ -577,14 +682,22 @@ hipError_t launch_gemm_nt_f16x3(const float* A, const float* B, _Float16* Bp, fl
 // Scores of the listed rows again in fp32, written over S: S[row, c] = h_row . Ft[c] (Ft [K, d],
 // row c the folded column W_g C_c^T), or (h_row W_g) . C[c] with W_g [d, d_g] and C [K, d_g].
 // For rows the fp16 product could not represent; one block per listed row at a time.
+//
+// With partials (Sinkhorn's first row step fused into the product's epilogue): block b also
+// takes that row step on its rows and writes its column summaries to partials[b * K + c] (every
+// launched block writes its slot, also with no rows).
 __global__ __launch_bounds__(256) void exact_rows_kernel(
     const float* __restrict__ H, int d, const float* __restrict__ Ft, const float* __restrict__ W,
     const float* __restrict__ Cm, int dg, int K, const int32_t* __restrict__ list,
-    const int32_t* __restrict__ count, float* __restrict__ S, int ldS) {
+    const int32_t* __restrict__ count, float* __restrict__ S, int ldS,
+    float2* __restrict__ partials) {
   __shared__ float part[4][1024];  // d_g <= 1024
   __shared__ float zs[1024];
+  __shared__ float sc[1024];       // K <= 1024: the row's scores
+  __shared__ float red[2][4];
   const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
   const int cnt = *count;
+  float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, ps[4] = {0.f, 0.f, 0.f, 0.f};
   auto wave_sum = [](float s) __attribute__((always_inline)) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -604,7 +717,10 @@ __global__ __launch_bounds__(256) void exact_rows_kernel(
           for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(hv[e], fv[e], a[e]);
         }
         const float s = wave_sum((a[0] + a[1]) + (a[2] + a[3]));
-        if (l == 0) srow[c] = s;
+        if (l == 0) {
+          srow[c] = s;
+          sc[c] = s;
+        }
       }
     } else {
       float z[16];  // columns l + 64 q of z = h W_g, over this wave's rows k = wave + 4 i
@@ -628,21 +744,50 @@ __global__ __launch_bounds__(256) void exact_rows_kernel(
         float s = 0.f;
         for (int k = l; k < dg; k += 64) s = __builtin_fmaf(zs[k], cr[k], s);
         s = wave_sum(s);
-        if (l == 0) srow[c] = s;
+        if (l == 0) {
+          srow[c] = s;
+          sc[c] = s;
+        }
       }
     }
     __syncthreads();
+    if (partials) {  // u = -logsumexp_c S[row, c], then the columns' running summaries
+      float mx = -INFINITY;
+      for (int c = tid; c < K; c += 256) mx = fmaxf(mx, sc[c]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      if (l == 0) red[0][wave] = mx;
+      __syncthreads();
+      mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+      float sum = 0.f;
+      for (int c = tid; c < K; c += 256) sum += fast_exp2((sc[c] - mx) * kLog2e);
+      sum = wave_sum(sum);
+      if (l == 0) red[1][wave] = sum;
+      __syncthreads();
+      const float u = -(mx + __logf((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (tid + 256 * q < K) ms_merge(pm[q], ps[q], sc[tid + 256 * q] + u, 1.f);
+      __syncthreads();
+    }
+  }
+  if (partials) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (tid + 256 * q < K) partials[(int64_t)blockIdx.x * K + tid + 256 * q] = make_float2(pm[q], ps[q]);
   }
 }
+
+int exact_rows_blocks(int64_t n) { return n < 256 ? (int)n : 256; }
 
 hipError_t launch_exact_rows(const float* H, int d, const float* Ft, const float* W,
                              const float* Cm, int dg, int K, const int32_t* list,
                              const int32_t* count, int64_t n, float* S, int ldS,
-                             hipStream_t stream) {
-  const int64_t blocks = n < 256 ? n : 256;
+                             float2* partials, hipStream_t stream) {
+  const int blocks = exact_rows_blocks(n);
   if (blocks < 1) return hipSuccess;
   hipLaunchKernelGGL(exact_rows_kernel, dim3(blocks), dim3(256), 0, stream, H, d, Ft, W, Cm, dg,
-                     K, list, count, S, ldS);
+                     K, list, count, S, ldS, partials);
   return hipGetLastError();
 }
 
@@ -677,41 +822,6 @@ hipError_t launch_fill_f32(float* p, float value, int64_t count, hipStream_t str
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, stream, p, value, count);
   return hipGetLastError();
-}
-
-// ============================================================================ row layouts
-// A row of K scores is spread over LPR lanes; lane q of the row holds columns
-// 4q + 4*LPR*c + e (c < CPL, e < 4). Rows per wave: 64 / LPR.
-// Row reductions over the row's LPR lanes (an aligned group): within a 16-lane row by VALU
-// lane moves (pairs, quads, half-row mirror, row mirror: each step combines two disjoint
-// halves of the group so far), across rows by lane shuffles.
-template <int LPR>
-__device__ __forceinline__ float row_max(float x) {
-  if constexpr (LPR >= 2) x = fmaxf(x, dpp_move<0xB1>(x));
-  if constexpr (LPR >= 4) x = fmaxf(x, dpp_move<0x4E>(x));
-  if constexpr (LPR >= 8) x = fmaxf(x, dpp_move<0x141>(x));
-  if constexpr (LPR >= 16) x = fmaxf(x, dpp_move<0x140>(x));
-  if constexpr (LPR >= 32) x = fmaxf(x, shfl_xor_f(x, 16));
-  if constexpr (LPR >= 64) x = fmaxf(x, shfl_xor_f(x, 32));
-  return x;
-}
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-  if constexpr (LPR >= 2) x += dpp_move<0xB1>(x);
-  if constexpr (LPR >= 4) x += dpp_move<0x4E>(x);
-  if constexpr (LPR >= 8) x += dpp_move<0x141>(x);
-  if constexpr (LPR >= 16) x += dpp_move<0x140>(x);
-  if constexpr (LPR >= 32) x += shfl_xor_f(x, 16);
-  if constexpr (LPR >= 64) x += shfl_xor_f(x, 32);
-  return x;
-}
-
-// Merge two (max, sum) summaries of exp: sum_i exp(x_i) = exp(m) * s.
-__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
-  float M = fmaxf(m, m2);
-  if (M == -INFINITY) return;
-  s = s * fast_exp2((m - M) * kLog2e) + s2 * fast_exp2((m2 - M) * kLog2e);
-  m = M;
 }
 
 // ============================================================================ Sinkhorn pass
@@ -887,6 +997,13 @@ int lanes_per_row(int K) {
   int lpr = 1;
   while (lpr < 64 && 16 * lpr < K) lpr *= 2;
   return lpr;
+}
+
+hipError_t launch_sinkhorn_cols(const float2* partials, int nblocks, int64_t n, int K, float* v,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(sinkhorn_cols_kernel, dim3(K), dim3(256), 0, stream, partials, nblocks, K,
+                     log((double)n / (double)K), v);
+  return hipGetLastError();
 }
 
 hipError_t launch_sinkhorn_iter(const float* S, int64_t n, int K, int ldS, float* v,

@@ -68,7 +68,10 @@ size_t assign_carve(void* ws, int64_t n, int d, int d_g, int K, AssignWs* out) {
   w.Bp = c.take<_Float16>(2 * bmax);
   w.bscale = c.take<float>((size_t)std::max(K, d_g));
   w.v = c.take<float>((size_t)padded_k(K));
-  w.partials = c.take<float2>((size_t)sinkhorn_blocks(n, K) * K);
+  // column summaries: the Sinkhorn row pass's blocks, or the fused first step's row blocks of
+  // the score product (at most one per 128 rows) and the exact rows' blocks
+  const int64_t nparts = std::max<int64_t>(sinkhorn_blocks(n, K), (n + 127) / 128 + 256);
+  w.partials = c.take<float2>((size_t)nparts * K);
   w.flags = c.take<int32_t>((size_t)std::max<int64_t>(n, 1));
   w.nflags = c.take<int32_t>(1);
   if (out) *out = w;
@@ -254,32 +257,48 @@ int focus_assign(const float* hidden, const float* w_g, const float* centroids, 
   hipError_t e;
   // The n-row products run as fp16 pair products (inner dimension a multiple of 32), else as
   // the bf16 split product. Rows the fp16 products cannot represent (hidden values beyond
-  // fp16's range) are listed and their scores recomputed exactly before Sinkhorn.
-  bool listed = false;
-  auto product = [&](const float* a, const float* b, float* c, int64_t m, int nn, int kd,
-                     int ldc) -> hipError_t {
-    if (kd % 32 != 0) return launch_gemm_nt_f32(a, b, c, m, nn, kd, ldc, st);
-    listed = true;
-    return launch_gemm_nt_f16x3(a, b, w.Bp, w.bscale, c, m, nn, kd, ldc, w.flags, w.nflags, st);
-  };
+  // fp16's range) are listed by the product that yields S (or by the first, when only it runs
+  // on fp16), so no row is listed twice, and their scores recomputed exactly before Sinkhorn.
+  // When S comes from an fp16 product spanning K <= 256 columns per block, that product's
+  // epilogue also takes Sinkhorn's first row step (the exact rows add theirs).
   const bool fold = assign_folds(d, d_g, K);
+  const bool s_f16 = (fold ? d : d_g) % 32 == 0;
+  const bool fuse = sinkhorn_iters > 0 && s_f16 && K <= 256;
+  bool listed = false;
+  int64_t row_blocks = 0;
+  auto product = [&](const float* a, const float* b, float* c, int64_t m, int nn, int kd,
+                     int ldc, bool scores) -> hipError_t {
+    if (kd % 32 != 0) return launch_gemm_nt_f32(a, b, c, m, nn, kd, ldc, st);
+    const bool lists = scores || !s_f16;
+    listed = listed || lists;
+    return launch_gemm_nt_f16x3(a, b, w.Bp, w.bscale, c, m, nn, kd, ldc,
+                                lists ? w.flags : nullptr, w.nflags,
+                                scores && fuse ? w.partials : nullptr,
+                                scores && fuse ? &row_blocks : nullptr, st);
+  };
   e = launch_fill_i32(w.nflags, 0, 1, st);
   if (e == hipSuccess && fold) {
     // Bt = (W_g C^T)^T = C W_g^T  [K, d];  S = H Bt^T
     e = launch_gemm_nt_f32(centroids, w_g, w.Bt, K, d, d_g, d, st);
-    if (e == hipSuccess) e = product(hidden, w.Bt, w.S, n, K, d, ldS);
+    if (e == hipSuccess) e = product(hidden, w.Bt, w.S, n, K, d, ldS, true);
   } else if (e == hipSuccess) {
     // Bt = W_g^T [d_g, d];  Z = H W_g;  S = Z C^T
     e = launch_transpose_f32(w_g, w.Bt, d, d_g, st);
-    if (e == hipSuccess) e = product(hidden, w.Bt, w.Z, n, d_g, d, d_g);
-    if (e == hipSuccess) e = product(w.Z, centroids, w.S, n, K, d_g, ldS);
+    if (e == hipSuccess) e = product(hidden, w.Bt, w.Z, n, d_g, d, d_g, false);
+    if (e == hipSuccess) e = product(w.Z, centroids, w.S, n, K, d_g, ldS, true);
   }
   if (e == hipSuccess && listed)
     e = launch_exact_rows(hidden, d, fold ? w.Bt : nullptr, w_g, centroids, d_g, K, w.flags,
-                          w.nflags, n, w.S, ldS, st);
+                          w.nflags, n, w.S, ldS, fuse ? w.partials + row_blocks * K : nullptr,
+                          st);
   if (e == hipSuccess) e = launch_fill_f32(w.v, 0.f, K, st);
+  int t0 = 0;
+  if (e == hipSuccess && fuse) {
+    e = launch_sinkhorn_cols(w.partials, (int)(row_blocks + exact_rows_blocks(n)), n, K, w.v, st);
+    t0 = 1;
+  }
   const int nblk = sinkhorn_blocks(n, K);
-  for (int t = 0; t < sinkhorn_iters && e == hipSuccess; ++t)
+  for (int t = t0; t < sinkhorn_iters && e == hipSuccess; ++t)
     e = launch_sinkhorn_iter(w.S, n, K, ldS, w.v, w.partials, nblk, st);
   if (e == hipSuccess) e = launch_topk(w.S, w.v, n, K, ldS, top_k, groups, st);
   if (e == hipSuccess && col_potential)
@@ -522,7 +541,10 @@ size_t train_carve(void* ws, int64_t n, int d, int d_g, int K, int Hq, int iters
   w.Z = c.take<float>((size_t)n * d_g);
   w.S = c.take<float>((size_t)n * K4);
   w.vs = c.take<float>((size_t)(iters + 1) * K4);
-  w.partials = c.take<float2>((size_t)sinkhorn_blocks(n, K) * K);
+  // column summaries: the Sinkhorn row pass's blocks, or the fused first step's row blocks of
+  // the score product (at most one per 128 rows) and the exact rows' blocks
+  const int64_t nparts = std::max<int64_t>(sinkhorn_blocks(n, K), (n + 127) / 128 + 256);
+  w.partials = c.take<float2>((size_t)nparts * K);
   w.gh = c.take<__bf16>((size_t)n * KP);
   w.gl = c.take<__bf16>((size_t)n * KP);
   w.D = c.take<float>((size_t)n * Hq);

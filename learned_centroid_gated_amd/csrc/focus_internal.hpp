@@ -132,16 +132,25 @@ hipError_t launch_topk(const float* S, const float* v, int64_t n, int K, int ldS
 // splits (three fp16 MFMA part products). Needs Kd % 32 == 0. Bp (2 N Kd fp16) and bscale (N
 // floats) are scratch for B's scaled planes. Rows of A whose outputs are not finite (an
 // element beyond fp16's range, or not finite) are appended to flags (nflags counts them) when
-// flags is given.
+// flags is given. With col_partials (N <= 256): the epilogue also takes Sinkhorn's first row
+// step and writes one (max, sum) column summary row per row block, *row_blocks of them, to
+// col_partials [*row_blocks, N]; listed rows stay out of them.
 hipError_t launch_gemm_nt_f16x3(const float* A, const float* B, _Float16* Bp, float* bscale,
                                 float* C, int64_t M, int N, int Kd, int ldc, int32_t* flags,
-                                int32_t* nflags, hipStream_t stream);
+                                int32_t* nflags, float2* col_partials, int64_t* row_blocks,
+                                hipStream_t stream);
 // S[row, :K] in fp32 for the rows listed in list[0..*count): h_row . Ft[c] when Ft ([K, d]) is
-// given, else (h_row W) . Cm[c] with W [d, d_g] and Cm [K, d_g]. n: the list's capacity.
+// given, else (h_row W) . Cm[c] with W [d, d_g] and Cm [K, d_g]. n: the list's capacity. With
+// partials: Sinkhorn's first row step on those rows too, one column summary row per launched
+// block (exact_rows_blocks(n) of them) at partials [blocks, K].
+int exact_rows_blocks(int64_t n);
 hipError_t launch_exact_rows(const float* H, int d, const float* Ft, const float* W,
                              const float* Cm, int dg, int K, const int32_t* list,
                              const int32_t* count, int64_t n, float* S, int ldS,
-                             hipStream_t stream);
+                             float2* partials, hipStream_t stream);
+// Sinkhorn's column step v_c = log(n / K) - logsumexp over the nblocks column summaries.
+hipError_t launch_sinkhorn_cols(const float2* partials, int nblocks, int64_t n, int K, float* v,
+                                hipStream_t stream);
 hipError_t launch_fill_f32(float* p, float value, int64_t count, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t count, hipStream_t stream);
 
