@@ -157,7 +157,11 @@ constexpr int wgs_per_cu() {
   return 2 * 2 * sizeof(Smem) <= 160 * 1024 ? 2 : 1;
 }
 
-template <int DH, int KP, bool BWD>
+// SH (T <= 32, every wave holding the same tokens): the affinity and gate of each (token, key)
+// pair are computed once per workgroup rather than once per head: wave w takes keys
+// 16 w .. 16 w + 15 of the tile against all T tokens on the 16x16x32 bf16 MFMA, turns them into
+// gate terms and leaves them in LDS for every wave's rows.
+template <int DH, int KP, bool BWD, bool SH>
 __global__ __launch_bounds__(256, (wgs_per_cu<TrainQSmem<DH, KP>>())) void train_q_kernel(const TrainArgs a) {
   using Smem = TrainQSmem<DH, KP>;
   constexpr int CH = DH / 8, RB = 2 * DH;     // 16-byte chunks and bytes per K/V row
@@ -168,6 +172,10 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainQSmem<DH, KP>>())) void train
   constexpr int INSTG = KT * CHG / 64 / 4;    // per wave per soft-assignment plane tile
   static_assert(INSTS >= 1 && INSTG >= 1, "tile copies");
   __shared__ __attribute__((aligned(1024))) Smem smem[2];
+  static_assert(!SH || KP >= 32, "shared gates take 32-group k-steps");
+  constexpr int GS = KT + 4;  // shared gate rows: one per token, padded against bank conflicts
+  __shared__ __attribute__((aligned(16))) float gate_s[SH ? 32 : 1][SH ? GS : 1];
+  __shared__ __attribute__((aligned(16))) float gsig_s[(SH && BWD) ? 32 : 1][(SH && BWD) ? GS : 1];
 
   const int tid = threadIdx.x, l = tid & 63, jq = l & 31, hg = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -207,11 +215,30 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainQSmem<DH, KP>>())) void train
       for (int s = 0; s < NS; ++s) dreg[s] = *(const bf16x8_t*)(dp + 16 * s);
     }
   }
-  bf16x8_t gqh[KS], gql[KS];  // the token's soft assignment, groups 16 s + 8 hg .. + 7
+  bf16x8_t gqh[SH ? 1 : KS], gql[SH ? 1 : KS];  // the token's soft assignment, groups 16 s + 8 hg .. + 7
+  if constexpr (!SH) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    gqh[s] = *(const bf16x8_t*)(a.gh + (int64_t)qrow * KP + 16 * s + 8 * hg);
-    gql[s] = *(const bf16x8_t*)(a.gl + (int64_t)qrow * KP + 16 * s + 8 * hg);
+    for (int s = 0; s < KS; ++s) {
+      gqh[s] = *(const bf16x8_t*)(a.gh + (int64_t)qrow * KP + 16 * s + 8 * hg);
+      gql[s] = *(const bf16x8_t*)(a.gl + (int64_t)qrow * KP + 16 * s + 8 * hg);
+    }
+  }
+  // SH: the B operand of the shared affinity product, token 16 tt + l % 16 of the tile at groups
+  // 32 s + 8 (l / 16) .. + 7 (zero past the tile's tokens)
+  constexpr int KS2 = KP / 32;
+  bf16x8_t gbh[SH ? 2 : 1][SH ? KS2 : 1], gbl[SH ? 2 : 1][SH ? KS2 : 1];
+  if constexpr (SH) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tk = 16 * tt + (l & 15);
+      const bool ok = tk < a.T && q0 + tk < q1;
+#pragma unroll
+      for (int s = 0; s < KS2; ++s) {
+        const int64_t off = (int64_t)(ok ? q0 + tk : 0) * KP + 32 * s + 8 * (l >> 4);
+        gbh[tt][s] = ok ? *(const bf16x8_t*)(a.gh + off) : bf16x8_t{};
+        gbl[tt][s] = ok ? *(const bf16x8_t*)(a.gl + off) : bf16x8_t{};
+      }
+    }
   }
   float lse2 = 0.f, drow = 0.f;
   if constexpr (BWD) {
@@ -321,9 +348,44 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainQSmem<DH, KP>>())) void train
           pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dreg[s], pacc[kb], 0, 0, 0);
         }
       }
+    // SH: this wave's share of the workgroup's gate tile, ahead of the score product so the
+    // barrier below finds it done
+    if constexpr (SH) {
+      if (far_any) {
+        const int krow = 16 * wave + (l & 15);  // key row of the tile
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if (16 * tt >= a.T) break;
+          f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS2; ++s) {
+            const int cc = 4 * s + (l >> 4);  // 16-byte chunk of the key's plane rows
+            const uint32_t ga = (uint32_t)(krow * RBG + ((cc ^ (swz(krow) % CHG)) * 16)) + par;
+            const bf16x8_t hf = *(const bf16x8_t*)(lds + offsetof(Smem, gh) + ga);
+            const bf16x8_t lf = *(const bf16x8_t*)(lds + offsetof(Smem, gl) + ga);
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hf, gbh[tt][s], a4, 0, 0, 0);
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hf, gbl[tt][s], a4, 0, 0, 0);
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf, gbh[tt][s], a4, 0, 0, 0);
+          }
+          // element i: key 16 wave + 4 (l / 16) + i, token 16 tt + l % 16
+          f32x4_t g4, s4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float l2s, sn;
+            gate_terms(a.lam * (a4[i] - 0.5f), l2s, sn);
+            g4[i] = l2s;
+            s4[i] = sn;
+          }
+          const int tk = 16 * tt + (l & 15), kc = 16 * wave + 4 * (l >> 4);
+          *(f32x4_t*)&gate_s[tk][kc] = g4;
+          if constexpr (BWD) *(f32x4_t*)&gsig_s[tk][kc] = s4;
+        }
+      }
+    }
+
     // A^T = G_k g_q^T from the two-part planes (hi hi + hi lo + lo hi)
     f32x16_t aacc[2] = {f32x16_t{}, f32x16_t{}};
-    if (far_any) {
+    if (!SH && far_any) {
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -334,6 +396,23 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainQSmem<DH, KP>>())) void train
           aacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, gql[s], aacc[kb], 0, 0, 0);
           aacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, gqh[s], aacc[kb], 0, 0, 0);
         }
+    }
+
+    // SH: every wave's gate terms are in LDS; this lane's row reads its token's
+    f32x4_t gv[SH ? 2 : 1][SH ? 4 : 1], sv[(SH && BWD) ? 2 : 1][(SH && BWD) ? 4 : 1];
+    if constexpr (SH) {
+      if (far_any) {
+        __syncthreads();
+        if (!all_near) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              gv[kb][q4] = *(const f32x4_t*)&gate_s[tok][kb * 32 + 8 * q4 + 4 * hg];
+              if constexpr (BWD) sv[kb][q4] = *(const f32x4_t*)&gsig_s[tok][kb * 32 + 8 * q4 + 4 * hg];
+            }
+        }
+      }
     }
 
     // gated logits in log2 units; element v of tile kb is key kb*32 + 8*(v/4) + 4*hg + v%4
@@ -349,7 +428,12 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainQSmem<DH, KP>>())) void train
         if (!all_near) {
           if (all_far || dd >= window) {
             float l2s;
-            gate_terms(a.lam * (aacc[kb][vi] - 0.5f), l2s, sn);
+            if constexpr (SH) {
+              l2s = gv[kb][vi >> 2][vi & 3];
+              if constexpr (BWD) sn = sv[kb][vi >> 2][vi & 3];
+            } else {
+              gate_terms(a.lam * (aacc[kb][vi] - 0.5f), l2s, sn);
+            }
             xx += l2s;
           }
           if (!all_far && dd < 0) xx = -INFINITY;
@@ -767,7 +851,15 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainKSmem<DH, KP, TQ>>())) void t
 template <int DH, int KP, bool BWD>
 static void train_q_launch(const TrainArgs& a, hipStream_t stream) {
   const int64_t blocks = xcd_grid((int64_t)a.Hkv * a.items);
-  hipLaunchKernelGGL((train_q_kernel<DH, KP, BWD>), dim3(blocks), dim3(256), 0, stream, a);
+  // shared gates where every wave holds the same tokens and the tiles already take one
+  // workgroup per CU (the gate tile then costs no occupancy)
+  if constexpr (KP >= 64) {
+    if (a.T <= 32) {
+      hipLaunchKernelGGL((train_q_kernel<DH, KP, BWD, true>), dim3(blocks), dim3(256), 0, stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((train_q_kernel<DH, KP, BWD, false>), dim3(blocks), dim3(256), 0, stream, a);
 }
 
 template <bool BWD>

@@ -71,6 +71,8 @@ CASES = [
     (640, 32, 8, 8, 16, 2, 64, 3, 1, 12.0, 5.0),
     (520, 96, 16, 16, 12, 12, 64, 3, 700, 4.0, 4.0),   # window >= n: no far pair
     (400, 64, 16, 8, 4, 2, 128, 2, 16, 0.0, 4.0),      # lambda 0: a constant gate
+    (600, 128, 64, 64, 16, 4, 128, 2, 48, 6.0, 4.0),   # G 4, 32 tokens, K 64: the 32K shape
+    (530, 64, 32, 100, 16, 2, 64, 3, 20, -4.0, 3.0),   # G 8, 16 tokens, K 100, head size 64
 ]
 
 
