@@ -739,6 +739,11 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainKSmem<DH, KP, TQ>>())) void t
     const bool all_far = t0 - kw_hi >= window;  // every pair far (and causal)
     const Smem& sm = *(const Smem*)(lds + par);
     f32x16_t aacc = f32x16_t{};
+    // T <= 32: a lane's rows 8 j + 4 hg + e of a block hold tokens (8 j + 4 hg + e) % T, so row
+    // groups j >= JD repeat groups j % JD, and block 1 repeats block 0: the gate terms of block
+    // 0's first JD groups serve every row
+    constexpr int JD = T >= 32 ? 4 : (T >= 8 ? T / 8 : 1);
+    float gl2[T <= 32 ? 4 * JD : 1], gsn[T <= 32 ? 4 * JD : 1];
 #pragma unroll
     for (int b = 0; b < QR / 32; ++b) {
       // S = Q K^T and dP = dO V^T for rows 32 b .. 32 b + 31 (M) and the wave's keys (N)
@@ -763,6 +768,10 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainKSmem<DH, KP, TQ>>())) void t
           aacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, gkl[s], aacc, 0, 0, 0);
           aacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, gkh[s], aacc, 0, 0, 0);
         }
+        if constexpr (T <= 32) {
+#pragma unroll
+          for (int i = 0; i < 4 * JD; ++i) gate_terms(a.lam * (aacc[i] - 0.5f), gl2[i], gsn[i]);
+        }
       }
       // element v is row 32 b + 8 (v / 4) + 4 hg + v % 4 of the tile, key = this lane's key
       bf16x8_t fb[2];
@@ -780,7 +789,12 @@ __global__ __launch_bounds__(256, (wgs_per_cu<TrainKSmem<DH, KP, TQ>>())) void t
           float f = 0.f;
           if ((all_far || dd >= window) && qi < a.n && kvalid) {
             float l2s, sn;
-            gate_terms(a.lam * (aacc[vi] - 0.5f), l2s, sn);
+            if constexpr (T <= 32) {
+              l2s = gl2[4 * (j % JD) + e];
+              sn = gsn[4 * (j % JD) + e];
+            } else {
+              gate_terms(a.lam * (aacc[vi] - 0.5f), l2s, sn);
+            }
             const float p = fast_exp2(sacc[vi] * a.sl2 + l2s - l4[e]);
             f = p * (pacc[vi] - d4[e]) * a.lam * sn;
           }
