@@ -53,6 +53,9 @@ CASES = [
     (300, 96, 64, 1024, 4, 2, 64),
     (4097, 512, 128, 64, 2, 5, 64),
     (2000, 256, 16, 8, 8, 3, 8),
+    # one iteration: the potentials come from the score product's fused first row step alone
+    (4096, 512, 128, 64, 2, 1, 64),     # folded, 128-column tiles
+    (3001, 64, 32, 256, 1, 1, 40),      # two products, 256-column tiles
 ]
 
 
