@@ -214,6 +214,25 @@ def prefill_bench(c, steps, warmup, hip, capture=False):
     wall = time.time() - wall0
     total_ms = start.elapsed_time(end)
     ms = total_ms / steps
+    # the same step replayed from a HIP graph (its launches captured once), checked bit-exact
+    # against the last eager step: what the step costs without host launch overhead
+    out_eager, groups_eager = out.clone(), groups.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_eager.view(torch.int16)), "graph replay differs"
+    assert torch.equal(groups, groups_eager), "graph replay differs"
+    del out_eager, groups_eager
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end) / steps
+    del graph
+    log(f"[bench]   replayed from a HIP graph: {graph_ms:.3f} ms/step")
     cap = None
     if capture:
         # what the oracle leg needs to check this very step: its inputs, its memberships and
@@ -243,6 +262,7 @@ def prefill_bench(c, steps, warmup, hip, capture=False):
     res = {
         "workload": c.name, "n": c.n, "ms_per_step": ms, "wall_s": wall, "steps": steps,
         "tokens_per_s": c.n / (ms / 1e3),
+        "graph_ms_per_step": graph_ms, "graph_tokens_per_s": c.n / (graph_ms / 1e3),
         "assign_ms": float(assign_ms), "bucket_ms": float(bucket_ms),
         "attention_stage_ms": stage_ms,
         "allowed_pairs": pairs, "window_pairs": wpairs, "group_pairs": gpairs,
@@ -519,6 +539,25 @@ def decode_bench(c, steps, warmup):
     out_ref = out.clone()
     focus_decode(qd, q_groups, t["k"], t["v"], lens, cache_groups, off, idx, c.K, c.window,
                  out=out_ref, lse=lse)
+
+    # the same step replayed from a HIP graph: the launch gaps between its three kernels go
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16)), "graph replay differs"
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    res["graph_us_per_step"] = s.elapsed_time(e) * 1e3 / steps
+    log(f"[bench]   decode replayed from a HIP graph {res['graph_us_per_step']:.1f} us/step")
+    del graph
 
     # the same step over a paged cache: 16-token pages scattered through one pool in a seeded
     # random order (focus_decode_paged), checked equal to the unpaged step
