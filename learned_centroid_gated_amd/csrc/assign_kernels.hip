@@ -608,7 +608,7 @@ __global__ __launch_bounds__(64 * WAVES, NT > 4 ? 2 : 4) void gemm_nt_f16x3_kern
       ms_merge(m, sm, __uint_as_float(pm[1]), __uint_as_float(ps[1]));
       if (g == 0) red[wave * (32 * NT) + t * 32 + j] = make_float2(m, sm);
     }
-    __syncthreads();
+    lds_barrier();  // LDS only: the score stores above need not land before the merge
     for (int c = tid; c < 32 * NT && c < N; c += 64 * WAVES) {
       float m = red[c].x, sm = red[c].y;
 #pragma unroll
