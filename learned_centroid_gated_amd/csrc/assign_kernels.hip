@@ -708,18 +708,30 @@ __global__ __launch_bounds__(256) void exact_rows_kernel(
     const float* h = H + row * d;
     float* srow = S + row * ldS;
     if (Ft) {
-      for (int c = wave; c < K; c += 4) {  // a wave per column, lanes over d (d % 4 == 0)
-        const float* f = Ft + (int64_t)c * d;
-        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-        for (int k = 4 * l; k < d; k += 256) {
-          const f32x4_t hv = *(const f32x4_t*)(h + k), fv = *(const f32x4_t*)(f + k);
+      // a wave takes 8 columns per pass over h, lanes over d (d % 4 == 0); each column's sum
+      // runs in the same order as one column at a time
+      for (int c0 = 8 * wave; c0 < K; c0 += 32) {
+        f32x4_t a[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(hv[e], fv[e], a[e]);
+        for (int cc = 0; cc < 8; ++cc) a[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int k = 4 * l; k < d; k += 256) {
+          const f32x4_t hv = *(const f32x4_t*)(h + k);
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            if (c0 + cc < K) {
+              const f32x4_t fv = *(const f32x4_t*)(Ft + (int64_t)(c0 + cc) * d + k);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[cc][e] = __builtin_fmaf(hv[e], fv[e], a[cc][e]);
+            }
+          }
         }
-        const float s = wave_sum((a[0] + a[1]) + (a[2] + a[3]));
-        if (l == 0) {
-          srow[c] = s;
-          sc[c] = s;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const float s = wave_sum((a[cc][0] + a[cc][1]) + (a[cc][2] + a[cc][3]));
+          if (l == 0 && c0 + cc < K) {
+            srow[c0 + cc] = s;
+            sc[c0 + cc] = s;
+          }
         }
       }
     } else {

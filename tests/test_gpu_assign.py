@@ -132,6 +132,27 @@ def test_assign_hidden_beyond_fp16_range(n, d, dg, K, top_k, iters):
     _check_groups(g, ref, ref["S"] + ref["v"][None, :])
 
 
+@pytest.mark.parametrize("n,d,dg,K,top_k,iters", [(2500, 512, 128, 100, 2, 3),
+                                                   (2100, 256, 32, 128, 1, 2)])
+def test_assign_every_row_beyond_fp16_range(n, d, dg, K, top_k, iters):
+    """Every token carries one hidden value beyond fp16's range in a damped channel, so the
+    fp16 score products list all of them and every score row is recomputed in fp32 (folded
+    plan with K not a multiple of the eight columns a wave takes per pass; two-product plan).
+    Groups and potentials must match the oracle."""
+    say(f"assign every row beyond fp16 range n={n} d={d} dg={dg} K={K}")
+    a = assign_inputs(n, d, dg, K, K, index=0, salt=11 * n + K)
+    h, w = a["hidden"].copy(), a["w_g"].copy()
+    w[:3] *= np.float32(1e-4)
+    rs = np.random.default_rng(n + K)
+    ch = rs.integers(0, 3, n)
+    h[np.arange(n), ch] = (rs.choice([-1.0, 1.0], n) * rs.uniform(7e4, 2e5, n)).astype(np.float32)
+    ref = assign_ref(h, w, a["centroids"], top_k, iters)
+    assert np.abs(ref["S"]).max() < 50.0
+    g, v = _run(h, w, a["centroids"], top_k, iters)
+    np.testing.assert_allclose(v, ref["v"], rtol=0, atol=2e-5)
+    _check_groups(g, ref, ref["S"] + ref["v"][None, :])
+
+
 def test_assign_deterministic():
     a = assign_inputs(5000, 256, 64, 32, 32, index=0, salt=77)
     g1, v1 = _run(a["hidden"], a["w_g"], a["centroids"], 2, 3)
