@@ -10,23 +10,49 @@
 // Three steps. A list kernel finds, per sequence, the window and each query group's slice of
 // its bucketed memberships (the plan), then resolves the virtual list into key positions once
 // per sequence (-1 for members that a lower shared query group owns). The partial kernel cuts
-// each list into `splits` pieces; its blocks read every listed key's K and V rows, all kv heads
-// of a token at once where the head count allows, and keep a running (max, sum, O) per query
-// head.
+// each list into `splits` pieces (chosen from the batch shape); its blocks read every listed
+// key's K and V rows, all kv heads of a token at once where the head count allows, and keep a
+// running (max, sum, O) per query head.
 // A combine kernel merges the pieces by log-sum-exp. The path is HBM-bound: every allowed key
 // costs one K row and one V row per kv head.
 #include "focus_internal.hpp"
 
 namespace focus {
 
-constexpr int kDecHeads = 4;     // query heads per block
-constexpr int kDecInfo = 12;     // per-sequence plan: lo, nl, -, then (segment start, count) x 4
-constexpr int kDecSplits = 16;   // key-list pieces per (sequence, head group)
-constexpr int kListBlocks = 32;  // list-resolution blocks per sequence (grid-stride over the list)
+constexpr int kDecHeads = 4;        // query heads per block
+constexpr int kDecInfo = 12;        // per-sequence plan: lo, nl, -, then (segment start, count) x 4
+constexpr int kDecBlocks = 512;     // partial-kernel blocks aimed for: two per compute unit
+constexpr int kDecMaxSplits = 256;  // key-list pieces per (sequence, head group), at most
+constexpr int kListBlocks = 32;     // list-resolution blocks per sequence (grid-stride over the list)
 
+// Query heads per unit (hpb), units per block (upb) and blocks of units per sequence (nub) of
+// the partial kernel. A unit is up to kDecHeads query heads of one kv head; a block's lane
+// groups (16 at d_head 128, 32 at 64) split into upb units, upb the largest power of two that
+// divides the sequence's unit count.
+struct DecodeUnits {
+  int hpb, upb, nub;
+};
+DecodeUnits decode_units(int Hq, int G, int dh) {
+  DecodeUnits u{};
+  u.hpb = G < kDecHeads ? G : kDecHeads;
+  const int units = Hq / u.hpb, ng = dh == 128 ? 16 : 32;
+  int g = ng;
+  while (units % g != 0) g /= 2;  // ng is a power of two: the largest common power of two
+  u.upb = g;
+  u.nub = units / g;
+  return u;
+}
+
+// Pieces per sequence: as many as keep the grid within kDecBlocks blocks. Every piece has the
+// same length, so with at most two blocks per compute unit no unit runs a third piece after the
+// others have finished; and two resident blocks of long pieces stream the scattered K/V rows
+// faster than four of half the length (measured on the 64 x 65536 decode).
 int decode_splits(const DecodeShape& s) {
-  (void)s;
-  return kDecSplits;
+  if (s.B < 1 || s.Hq < 1 || s.G < 1 || s.Hq % s.G != 0) return 1;
+  const int64_t per = (int64_t)s.B * decode_units(s.Hq, s.G, s.dh).nub;
+  if (per >= kDecBlocks) return 1;
+  const int64_t sp = kDecBlocks / per;
+  return (int)(sp < kDecMaxSplits ? sp : kDecMaxSplits);
 }
 
 // ============================================================================ plan
@@ -222,15 +248,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // 16-byte chunk of the key's K and V rows; the dot products are reduced across the 16 lanes
 // with row moves, and a running (max, sum, O) per head absorbs the key. A lane group keeps U
 // keys' rows in flight and loads the positions of its next U keys before absorbing the
-// current ones.
+// current ones (three rather than four in flight measured faster on the scattered rows).
 template <int DH>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
   constexpr int CHK = DH / 8;          // 16-byte chunks per row: lanes per key
   constexpr int KPW = kWave / CHK;     // lane groups per wave
   constexpr int NG = 4 * KPW;          // lane groups per block
   constexpr int HD = kDecHeads;
-  constexpr int U = 4;                 // keys in flight per lane group
-  static_assert(U == 4, "the batch maximum below takes four keys");
+  constexpr int U = 3;                 // keys in flight per lane group
   __shared__ float red_o[NG][HD][DH];
   __shared__ float red_ml[NG][HD][2];
 
@@ -326,7 +351,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
     bool bump = false;
 #pragma unroll
     for (int hh = 0; hh < HD; ++hh) {
-      bmax[hh] = fmaxf(fmaxf(sc[0][hh], sc[1][hh]), fmaxf(sc[2][hh], sc[3][hh]));
+      bmax[hh] = sc[0][hh];
+#pragma unroll
+      for (int u = 1; u < U; ++u) bmax[hh] = fmaxf(bmax[hh], sc[u][hh]);
       bump = bump || bmax[hh] > m_run[hh] + 8.f;
     }
     if (bump) {
@@ -395,37 +422,28 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   }
 }
 
+// One block per (sequence, query head), a thread per output dimension: the pieces' partials
+// merged by log-sum-exp in piece order, (max, sum) pairs read first for the common maximum.
 template <int DH>
 __global__ __launch_bounds__(DH) void decode_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
-                                                            int Hq, int Hkv, int G, int splits,
-                                                            uint16_t* __restrict__ out,
+                                                            int splits, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;  // b * Hq + hq
-  (void)Hq;
-  (void)Hkv;
-  (void)G;
   const int d = threadIdx.x;
-  (void)splits;  // always kDecSplits
-  float m[kDecSplits], sm[kDecSplits], po[kDecSplits];
-#pragma unroll
-  for (int s = 0; s < kDecSplits; ++s) {  // every load in flight at once
-    const int64_t pi = bh * kDecSplits + s;
-    const float2 ml = *(const float2*)&part_ml[pi * 2];
-    m[s] = ml.x;
-    sm[s] = ml.y;
-    po[s] = part_o[pi * DH + d];
-  }
+  const float2* ml = (const float2*)part_ml + bh * splits;
+  const float* po = part_o + bh * splits * DH + d;
   float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kDecSplits; ++s) M = fmaxf(M, m[s]);
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s].x);
   float den = 0.f, acc = 0.f;
   if (M != -INFINITY) {
-#pragma unroll
-    for (int s = 0; s < kDecSplits; ++s) {
-      const float w = m[s] == -INFINITY ? 0.f : fast_exp2(m[s] - M);
-      den += w * sm[s];
-      acc += w * po[s];
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) {
+      const float2 m = ml[s];
+      const float w = m.x == -INFINITY ? 0.f : fast_exp2(m.x - M);
+      den += w * m.y;
+      acc += w * po[(int64_t)s * DH];
     }
   }
   float o = den > 0.f ? acc / den : 0.f;
@@ -441,7 +459,7 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
                          uint16_t* out, float* lse, hipStream_t stream, const DecodePaging* pg,
                          const DecodeSlots* sl) {
   const int64_t per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
-  if (s.splits != kDecSplits) return hipErrorInvalidValue;
+  if (s.splits < 1 || s.splits > kDecMaxSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * kListBlocks), dim3(256),
                      0, stream, q_groups, cache_groups, cache_len, cache_off, cache_idx, info,
                      s.Lmax, s.K, s.top_k, s.window, per_seq, sl ? sl->seg_len : nullptr,
@@ -465,24 +483,20 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   a.sl2 = s.scale * kLog2e;
   a.part_o = part_o;
   a.part_ml = part_ml;
-  a.hpb = s.G < kDecHeads ? s.G : kDecHeads;
-  {
-    const int units = s.Hq / a.hpb, ng = s.dh == 128 ? 16 : 32;  // lane groups per block
-    int g = ng;
-    while (units % g != 0) g /= 2;  // ng is a power of two: the largest common power of two
-    a.upb = g;
-  }
-  const int64_t blocks = xcd_grid((int64_t)s.B * (s.Hq / a.hpb / a.upb) * s.splits);
+  const DecodeUnits du = decode_units(s.Hq, s.G, s.dh);
+  a.hpb = du.hpb;
+  a.upb = du.upb;
+  const int64_t blocks = xcd_grid((int64_t)s.B * du.nub * s.splits);
   if (s.dh == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int64_t)s.B * s.Hq), dim3(128), 0, stream,
-                       part_o, part_ml, s.Hq, s.Hkv, s.G, s.splits, out, lse);
+                       part_o, part_ml, s.splits, out, lse);
   } else {
     hipLaunchKernelGGL(decode_partial_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int64_t)s.B * s.Hq), dim3(64), 0, stream,
-                       part_o, part_ml, s.Hq, s.Hkv, s.G, s.splits, out, lse);
+                       part_o, part_ml, s.splits, out, lse);
   }
   return hipGetLastError();
 }

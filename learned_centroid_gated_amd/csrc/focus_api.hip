@@ -733,6 +733,11 @@ size_t focus_decode_workspace_size(int B, int64_t Lmax, int Hq, int Hkv, int d_h
   (void)K;
   if (B < 0 || Lmax < 1 || Hq < 1 || Hkv < 1 || d_head < 1 || top_k < 1) return 0;
   DecodeShape s{};
+  s.B = B;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.G = Hq / Hkv;
+  s.dh = d_head;
   return decode_carve(nullptr, B, Lmax, Hq, d_head, top_k, decode_splits(s), nullptr);
 }
 

@@ -42,6 +42,24 @@ def test_decode_matches_oracle(B, L, Hq, Hkv, dh, K, k, w):
     check_attention(out, lse, o_ref, l_ref, "decode")
 
 
+@pytest.mark.parametrize("B", [200, 520])
+def test_decode_large_batch(B):
+    """Many short sequences: the key lists are cut into two pieces (200 sequences) or one
+    (520), so each sequence's partial covers its whole list; lengths from 1 to L."""
+    L, Hq, Hkv, dh, K, k, w = 50, 8, 2, 64, 4, 2, 8
+    say(f"decode large batch B={B} L={L} Hq={Hq} Hkv={Hkv} dh={dh} K={K} top_k={k} window={w}")
+    rng = np.random.default_rng(B)
+    t = qkv_inputs(L, Hq, Hkv, dh, index=0, salt=450 + B, lead=(B,))
+    cache_groups = np.stack([random_groups(L, K, k, rng) for _ in range(B)])
+    q_groups = np.stack([random_groups(1, K, k, rng)[0] for _ in range(B)])
+    lens = rng.integers(1, L + 1, B).astype(np.int32)
+    qd = np.stack([t["q"][b, lens[b] - 1] for b in range(B)])
+    out, lse = run_decode(bf16_dev(qd), i32_dev(q_groups), bf16_dev(t["k"]), bf16_dev(t["v"]),
+                          i32_dev(lens), i32_dev(cache_groups), K, w)
+    o_ref, l_ref = decode_ref(qd, q_groups, t["k"], t["v"], lens, cache_groups, w)
+    check_attention(out, lse, o_ref, l_ref, "decode, large batch")
+
+
 def test_decode_equals_last_prefill_row_on_gpu():
     from learned_centroid_gated_amd import focus_attention, focus_bucket
     L, Hq, Hkv, dh, K, k, w = 3000, 16, 4, 128, 32, 2, 128
