@@ -422,34 +422,64 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   }
 }
 
-// One block per (sequence, query head), a thread per output dimension: the pieces' partials
-// merged by log-sum-exp in piece order, (max, sum) pairs read first for the common maximum.
+// One block per (sequence, query head): the pieces' partials merged by log-sum-exp. The block's
+// threads take the pieces' (max, sum) pairs one each for the common maximum and the denominator,
+// then every output dimension's weighted sum is split over NT / DH groups of pieces (piece
+// g, g + NT / DH, ...), whose results are added in group order.
 template <int DH>
-__global__ __launch_bounds__(DH) void decode_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(512) void decode_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
                                                             int splits, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
+  constexpr int NT = 512, NGRP = NT / DH, NW = NT / kWave;
+  static_assert(kDecMaxSplits <= NT, "one piece per thread for the (max, sum) pairs");
+  __shared__ float2 sml[kDecMaxSplits];
+  __shared__ float red[NW];
+  __shared__ float racc[NGRP][DH];
   const int64_t bh = blockIdx.x;  // b * Hq + hq
-  const int d = threadIdx.x;
-  const float2* ml = (const float2*)part_ml + bh * splits;
-  const float* po = part_o + bh * splits * DH + d;
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s].x);
-  float den = 0.f, acc = 0.f;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const float2 mine = tid < splits ? ((const float2*)part_ml)[bh * splits + tid]
+                                   : make_float2(-INFINITY, 0.f);
+  if (tid < splits) sml[tid] = mine;
+  float x = mine.x;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  if (l == 0) red[w] = x;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();  // red is reused below
+  float y = mine.x == -INFINITY ? 0.f : fast_exp2(mine.x - M) * mine.y;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) y += __shfl_xor(y, off);
+  if (l == 0) red[w] = y;
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) den += red[i];
+  const int d = tid % DH, g = tid / DH;
+  float acc = 0.f;
   if (M != -INFINITY) {
-#pragma unroll 8
-    for (int s = 0; s < splits; ++s) {
-      const float2 m = ml[s];
-      const float w = m.x == -INFINITY ? 0.f : fast_exp2(m.x - M);
-      den += w * m.y;
-      acc += w * po[(int64_t)s * DH];
+    const float* po = part_o + bh * splits * DH + d;
+#pragma unroll 4
+    for (int s = g; s < splits; s += NGRP) {
+      const float2 m = sml[s];
+      const float wt = m.x == -INFINITY ? 0.f : fast_exp2(m.x - M);
+      acc += wt * po[(int64_t)s * DH];
     }
   }
-  float o = den > 0.f ? acc / den : 0.f;
-  __bf16 ob = to_bf16(o);
-  out[bh * DH + d] = *(uint16_t*)&ob;
-  if (d == 0) lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  racc[g][d] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float a = racc[0][d];
+#pragma unroll
+    for (int i = 1; i < NGRP; ++i) a += racc[i][d];
+    const float o = den > 0.f ? a / den : 0.f;
+    __bf16 ob = to_bf16(o);
+    out[bh * DH + d] = *(uint16_t*)&ob;
+    if (d == 0) lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  }
 }
 
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
@@ -490,12 +520,12 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   if (s.dh == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int64_t)s.B * s.Hq), dim3(128), 0, stream,
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int64_t)s.B * s.Hq), dim3(512), 0, stream,
                        part_o, part_ml, s.splits, out, lse);
   } else {
     hipLaunchKernelGGL(decode_partial_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int64_t)s.B * s.Hq), dim3(64), 0, stream,
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int64_t)s.B * s.Hq), dim3(512), 0, stream,
                        part_o, part_ml, s.splits, out, lse);
   }
   return hipGetLastError();
