@@ -7,13 +7,13 @@
 // sees itself), then for each query group g_r the segment members at positions <= p - w'
 // whose lowest group shared with the query is g_r, so every allowed key appears once.
 //
-// Three steps. A list kernel finds, per sequence, the window and each query group's slice of
-// its bucketed memberships (the plan), then resolves the virtual list into key positions once
-// per sequence (-1 for members that a lower shared query group owns). The partial kernel cuts
-// each list into `splits` pieces (chosen from the batch shape); its blocks read every listed
-// key's K and V rows, all kv heads of a token at once where the head count allows, and keep a
-// running (max, sum, O) per query head.
-// A combine kernel merges the pieces by log-sum-exp. The path is HBM-bound: every allowed key
+// Two kernels. Each block of the partial kernel first finds its sequence's plan: where the
+// window starts and each query group's slice of the sequence's bucketed memberships (one wave per
+// query group). It then resolves its own piece of the virtual list into key positions in LDS (-1
+// for members that a lower shared query group owns), a chunk at a time, and reads every listed
+// key's K and V rows, all kv heads of a token at once where the head count allows, keeping a
+// running (max, sum, O) per query head. The pieces (`splits` per sequence, chosen from the batch
+// shape) are merged by log-sum-exp in a second kernel. The path is HBM-bound: every allowed key
 // costs one K row and one V row per kv head.
 #include "focus_internal.hpp"
 
@@ -23,7 +23,7 @@ constexpr int kDecHeads = 4;        // query heads per block
 constexpr int kDecInfo = 12;        // per-sequence plan: lo, nl, -, then (segment start, count) x 4
 constexpr int kDecBlocks = 512;     // partial-kernel blocks aimed for: two per compute unit
 constexpr int kDecMaxSplits = 256;  // key-list pieces per (sequence, head group), at most
-constexpr int kListBlocks = 32;     // list-resolution blocks per sequence (grid-stride over the list)
+constexpr int kDecChunk = 1024;     // list entries a partial block resolves into LDS at a time
 
 // Query heads per unit (hpb), units per block (upb) and blocks of units per sequence (nub) of
 // the partial kernel. A unit is up to kDecHeads query heads of one kv head; a block's lane
@@ -56,7 +56,7 @@ int decode_splits(const DecodeShape& s) {
 }
 
 // ============================================================================ plan
-// info[b] = (lo, nl, 0, seg_lo_0, cnt_0, ..., seg_lo_3, cnt_3): the window is positions
+// inf = (lo, nl, 0, seg_lo_0, cnt_0, ..., seg_lo_3, cnt_3): the window is positions
 // lo .. lo + nl - 1; query group r contributes the cnt_r members of its segment from index
 // seg_lo_r on (indices into the sequence's member list), those at positions <= p - w'. One
 // wave per query group finds the boundary with a 64-ary search: each step probes 64 evenly
@@ -79,133 +79,26 @@ __device__ __forceinline__ int64_t seg_search(const int32_t* __restrict__ member
   return lo_i - s0;
 }
 
-// list[b][vi] = key position of virtual list entry vi, or -1 when the entry is a member of a
-// query group that a lower shared query group owns (so every allowed key is listed once).
-// Every block first builds its sequence's plan (waves 0 .. top_k - 1 search one query group
-// each); the sequence's first block also stores it in info[b] for the partial kernel.
 // Memberships come bucketed (cache_off / cache_idx: offsets and one index list of capacity
 // Lmax * top_k per sequence) or, with seg_len, group-slotted (cache_idx holds seg_pos: a row of
 // gcap positions per (sequence, group), seg_len[b * K + g] of them in use). A listed position
-// outside [0, p] is skipped, and the list never exceeds its capacity per_seq.
-// With a page table the entry is the key's row in the shared page pool instead:
+// outside [0, p] is skipped, and a sequence's list never exceeds per_seq entries. With a page
+// table an entry is the key's row in the shared page pool instead:
 // table[b][pos / page] * page + pos % page, or -1 when the table entry is not a page of the pool.
-__global__ __launch_bounds__(256) void decode_list_kernel(const int32_t* __restrict__ q_groups,
-                                                          const int32_t* __restrict__ cache_groups,
-                                                          const int32_t* __restrict__ cache_len,
-                                                          const int32_t* __restrict__ cache_off,
-                                                          const int32_t* __restrict__ cache_idx,
-                                                          int32_t* __restrict__ info,
-                                                          int64_t Lmax, int K, int top_k,
-                                                          int64_t window, int64_t per_seq,
-                                                          const int32_t* __restrict__ seg_len,
-                                                          int gcap,
-                                                          const int32_t* __restrict__ table,
-                                                          int page, int64_t pages_per_seq,
-                                                          int64_t num_pages,
-                                                          int32_t* __restrict__ list) {
-  const int b = (int)(blockIdx.x / kListBlocks);
-  __shared__ int32_t inf[kDecInfo];
-  const int32_t* members = seg_len ? cache_idx + (int64_t)b * K * gcap
-                                   : cache_idx + (int64_t)b * Lmax * top_k;
-  int64_t L = cache_len[b];
-  if (L < 1) L = 1;
-  if (L > Lmax) L = Lmax;
-  const int64_t p = L - 1;
-  {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t wl = window > 1 ? window : 1;  // the new token always sees itself
-    const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
-    if (w < top_k) {
-      const int g = q_groups[(int64_t)b * top_k + w];
-      int64_t s0 = 0, s1 = 0;
-      if (g >= 0 && g < K) {
-        if (seg_len) {
-          int64_t n = seg_len[(int64_t)b * K + g];
-          n = n < 0 ? 0 : (n > gcap ? gcap : n);
-          s0 = (int64_t)g * gcap;
-          s1 = s0 + n;
-        } else {
-          const int32_t* off = cache_off + (int64_t)b * (K + 1);
-          s0 = off[g];
-          s1 = off[g + 1];
-          if (s0 < 0 || s1 < s0 || s1 > per_seq) s0 = s1 = 0;  // not a bucket of this capacity
-        }
-      }
-      const int64_t cnt = seg_search(members, s0, s1, p - wl, l);
-      if (l == 0) {
-        inf[3 + 2 * w] = (int32_t)s0;
-        inf[4 + 2 * w] = (int32_t)cnt;
-      }
-    } else if (threadIdx.x == 64 * 3) {  // a lane of a wave without a search (top_k < 4)
-      for (int rr = top_k; rr < 4; ++rr) {
-        inf[3 + 2 * rr] = 0;
-        inf[4 + 2 * rr] = 0;
-      }
-    }
-    if (threadIdx.x == 0) {
-      inf[0] = (int32_t)lo;
-      inf[1] = (int32_t)(p - lo + 1);
-      inf[2] = 0;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {  // the list holds at most per_seq entries
-      int64_t run = inf[1];
-      for (int r = 0; r < top_k; ++r) {
-        const int64_t room = per_seq - run;
-        if (inf[4 + 2 * r] > room) inf[4 + 2 * r] = (int32_t)room;
-        run += inf[4 + 2 * r];
-      }
-    }
-    __syncthreads();
-    if (blockIdx.x % kListBlocks == 0 && threadIdx.x < kDecInfo)
-      info[(int64_t)b * kDecInfo + threadIdx.x] = inf[threadIdx.x];
-  }
-  const int64_t lo = inf[0], nl = inf[1];
-  int64_t total = nl;
-  for (int r = 0; r < top_k; ++r) total += inf[4 + 2 * r];
-  for (int64_t vi = (blockIdx.x % kListBlocks) * 256 + threadIdx.x; vi < total;
-       vi += (int64_t)kListBlocks * 256) {
-    int pos = -1;
-    if (vi < nl) {
-      pos = (int)(lo + vi);
-    } else {
-      int qg[4];
-      for (int r = 0; r < top_k; ++r) qg[r] = q_groups[(int64_t)b * top_k + r];
-      int64_t rem = vi - nl;
-      for (int r = 0; r < top_k; ++r) {
-        const int64_t cnt = inf[4 + 2 * r];
-        if (rem < cnt) {
-          const int cand = members[inf[3 + 2 * r] + rem];
-          if (cand < 0 || cand > p) break;  // not a cached position: skipped
-          // owned by g_r unless the key also holds a lower query group
-          bool owned = true;
-          const int32_t* kg = cache_groups + ((int64_t)b * Lmax + cand) * top_k;
-          for (int r2 = 0; r2 < top_k; ++r2) {
-            const int g2 = qg[r2];
-            if (g2 >= 0 && g2 < K && g2 < qg[r])
-              for (int r3 = 0; r3 < top_k; ++r3) owned = owned && kg[r3] != g2;
-          }
-          pos = owned ? cand : -1;
-          break;
-        }
-        rem -= cnt;
-      }
-    }
-    if (table && pos >= 0) {
-      const int64_t pg = table[(int64_t)b * pages_per_seq + pos / page];
-      pos = (pg >= 0 && pg < num_pages) ? (int)(pg * page + pos % page) : -1;
-    }
-    list[(int64_t)b * per_seq + vi] = pos;
-  }
-}
-
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* kc;
   const uint16_t* vc;
-  const int32_t* info;
-  const int32_t* list;
-  int64_t per_seq;  // list capacity per sequence
+  const int32_t* q_groups;      // [B, top_k]
+  const int32_t* cache_groups;  // [B, Lmax, top_k]
+  const int32_t* cache_len;     // [B]
+  const int32_t* cache_off;     // [B, K + 1] (bucketed)
+  const int32_t* cache_idx;     // [B, Lmax * top_k] (bucketed) or seg_pos [B, K, gcap]
+  const int32_t* seg_len;       // [B, K] (group-slotted), else null
+  const int32_t* table;         // [B, pages_per_seq] (paged), else null
+  int64_t Lmax, window, pages_per_seq, num_pages;
+  int K, gcap, page;
+  int64_t per_seq;  // list entries per sequence, at most
   int B;
   int64_t seq_rows;  // rows between consecutive sequences' caches (0: list rows are pool rows)
   int Hq, Hkv, G, top_k, splits;
@@ -258,6 +151,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   constexpr int U = 3;                 // keys in flight per lane group
   __shared__ float red_o[NG][HD][DH];
   __shared__ float red_ml[NG][HD][2];
+  __shared__ int32_t inf[kDecInfo];
+  __shared__ int32_t qg_s[4];
+  __shared__ int32_t pos_s[kDecChunk];
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int c = l % CHK, grp = wave * KPW + l / CHK;  // chunk of the row, lane group
@@ -274,13 +170,100 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const int hq0 = (ub * upb + ul) * a.hpb, h = hq0 / a.G;
   const int nh = a.hpb;
 
-  const int32_t* inf = a.info + (int64_t)b * kDecInfo;
-  int64_t total = inf[1];
+  // ---- the sequence's plan (every block of the sequence finds the same one)
+  const int32_t* members = a.seg_len ? a.cache_idx + (int64_t)b * a.K * a.gcap
+                                     : a.cache_idx + (int64_t)b * a.Lmax * a.top_k;
+  int64_t L = a.cache_len[b];
+  if (L < 1) L = 1;
+  if (L > a.Lmax) L = a.Lmax;
+  const int64_t p = L - 1;
+  {
+    const int64_t wl = a.window > 1 ? a.window : 1;  // the new token always sees itself
+    const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
+    if (wave < a.top_k) {
+      const int g = a.q_groups[(int64_t)b * a.top_k + wave];
+      int64_t s0 = 0, s1 = 0;
+      if (g >= 0 && g < a.K) {
+        if (a.seg_len) {
+          int64_t n = a.seg_len[(int64_t)b * a.K + g];
+          n = n < 0 ? 0 : (n > a.gcap ? a.gcap : n);
+          s0 = (int64_t)g * a.gcap;
+          s1 = s0 + n;
+        } else {
+          const int32_t* off = a.cache_off + (int64_t)b * (a.K + 1);
+          s0 = off[g];
+          s1 = off[g + 1];
+          if (s0 < 0 || s1 < s0 || s1 > a.per_seq) s0 = s1 = 0;  // not a bucket of this capacity
+        }
+      }
+      const int64_t cnt = seg_search(members, s0, s1, p - wl, l);
+      if (l == 0) {
+        inf[3 + 2 * wave] = (int32_t)s0;
+        inf[4 + 2 * wave] = (int32_t)cnt;
+        qg_s[wave] = g;
+      }
+    } else if (tid == 64 * 3) {  // a lane of a wave without a search (top_k < 4)
+      for (int rr = a.top_k; rr < 4; ++rr) {
+        inf[3 + 2 * rr] = 0;
+        inf[4 + 2 * rr] = 0;
+      }
+    }
+    if (tid == 0) {
+      inf[0] = (int32_t)lo;
+      inf[1] = (int32_t)(p - lo + 1);
+      inf[2] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {  // the list holds at most per_seq entries
+      int64_t run = inf[1];
+      for (int r = 0; r < a.top_k; ++r) {
+        const int64_t room = a.per_seq - run;
+        if (inf[4 + 2 * r] > room) inf[4 + 2 * r] = (int32_t)room;
+        run += inf[4 + 2 * r];
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t lo = inf[0], nl = inf[1];
+  int64_t total = nl;
   for (int r = 0; r < a.top_k; ++r) total += inf[4 + 2 * r];
   const int64_t per = (total + a.splits - 1) / a.splits;
   const int64_t v0 = (int64_t)sp * per;
   const int64_t v1 = v0 + per < total ? v0 + per : total;
-  const int32_t* lst = a.list + (int64_t)b * a.per_seq;
+
+  // key position (or pool row) of virtual list entry vi, -1 for an entry that is dropped: a
+  // member of a query group that a lower shared query group owns, or not a cached position
+  auto entry = [&](int64_t vi) __attribute__((always_inline)) {
+    int pos = -1;
+    if (vi < nl) {
+      pos = (int)(lo + vi);
+    } else {
+      int64_t rem = vi - nl;
+      for (int r = 0; r < a.top_k; ++r) {
+        const int64_t cnt = inf[4 + 2 * r];
+        if (rem < cnt) {
+          const int cand = members[inf[3 + 2 * r] + rem];
+          if (cand < 0 || cand > p) break;  // not a cached position: skipped
+          // owned by g_r unless the key also holds a lower query group
+          bool owned = true;
+          const int32_t* kg = a.cache_groups + ((int64_t)b * a.Lmax + cand) * a.top_k;
+          for (int r2 = 0; r2 < a.top_k; ++r2) {
+            const int g2 = qg_s[r2];
+            if (g2 >= 0 && g2 < a.K && g2 < qg_s[r])
+              for (int r3 = 0; r3 < a.top_k; ++r3) owned = owned && kg[r3] != g2;
+          }
+          pos = owned ? cand : -1;
+          break;
+        }
+        rem -= cnt;
+      }
+    }
+    if (a.table && pos >= 0) {
+      const int64_t pg = a.table[(int64_t)b * a.pages_per_seq + pos / a.page];
+      pos = (pg >= 0 && pg < a.num_pages) ? (int)(pg * a.page + pos % a.page) : -1;
+    }
+    return pos;
+  };
 
   // this lane's slice of the query heads as bf16 pairs; scores are scaled after the reduction
   i32x4_t qr[HD];
@@ -302,27 +285,23 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const uint16_t* kbase = a.kc + (int64_t)b * a.seq_rows * kv_stride + (int64_t)h * DH + c * 8;
   const uint16_t* vbase = a.vc + (int64_t)b * a.seq_rows * kv_stride + (int64_t)h * DH + c * 8;
 
-  // entries v0 + slot + k * slots of the piece, U at a time
-  int pn[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t j = v0 + slot + (int64_t)u * slots;
-    pn[u] = j < v1 ? lst[j] : -1;
-  }
-  for (int64_t j0 = v0 + slot; j0 < v1; j0 += (int64_t)U * slots) {
+  // the piece a chunk at a time: its positions resolved into LDS by the whole block, then
+  // entries slot + k * slots of the chunk taken U at a time by each lane group
+  for (int64_t c0 = v0; c0 < v1; c0 += kDecChunk) {
+  const int cn = (int)(v1 - c0 < kDecChunk ? v1 - c0 : kDecChunk);
+  __syncthreads();  // every lane group is done with the previous chunk's positions
+  for (int i = tid; i < cn; i += 256) pos_s[i] = entry(c0 + i);
+  __syncthreads();
+  for (int i0 = slot; i0 < cn; i0 += U * slots) {
     int pk[U];
     i32x4_t kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      pk[u] = pn[u];
+      const int i = i0 + u * slots;
+      pk[u] = i < cn ? pos_s[i] : -1;
       const int64_t row = pk[u] >= 0 ? pk[u] : 0;
       kr[u] = *(const i32x4_t*)(kbase + row * kv_stride);
       vr[u] = *(const i32x4_t*)(vbase + row * kv_stride);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {  // positions of the next U keys, behind this batch's rows
-      const int64_t j = j0 + (int64_t)(U + u) * slots;
-      pn[u] = j < v1 ? lst[j] : -1;
     }
     // scores of the batch's U keys for every head (heads past nh are computed and ignored),
     // all before any reduction so the independent row-move chains interleave
@@ -384,6 +363,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
         for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pw, vf[e], o[hh][e]);
       }
     }
+  }
   }
 
   // ---- merge each unit's key slots and write this block's partial per head
@@ -485,24 +465,28 @@ __global__ __launch_bounds__(512) void decode_combine_kernel(const float* __rest
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
-                         int32_t* info, int32_t* list, float* part_o, float* part_ml,
-                         uint16_t* out, float* lse, hipStream_t stream, const DecodePaging* pg,
-                         const DecodeSlots* sl) {
-  const int64_t per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
+                         float* part_o, float* part_ml, uint16_t* out, float* lse,
+                         hipStream_t stream, const DecodePaging* pg, const DecodeSlots* sl) {
   if (s.splits < 1 || s.splits > kDecMaxSplits) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_list_kernel, dim3((int64_t)s.B * kListBlocks), dim3(256),
-                     0, stream, q_groups, cache_groups, cache_len, cache_off, cache_idx, info,
-                     s.Lmax, s.K, s.top_k, s.window, per_seq, sl ? sl->seg_len : nullptr,
-                     sl ? sl->gcap : 0, pg ? pg->table : nullptr, pg ? pg->page_size : 1,
-                     pg ? pg->pages_per_seq : 0, pg ? pg->num_pages : 0, list);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   DecodeArgs a{};
   a.q = q;
   a.kc = kc;
   a.vc = vc;
-  a.info = info;
-  a.list = list;
-  a.per_seq = per_seq;
+  a.q_groups = q_groups;
+  a.cache_groups = cache_groups;
+  a.cache_len = cache_len;
+  a.cache_off = cache_off;
+  a.cache_idx = cache_idx;
+  a.seg_len = sl ? sl->seg_len : nullptr;
+  a.gcap = sl ? sl->gcap : 0;
+  a.table = pg ? pg->table : nullptr;
+  a.page = pg ? pg->page_size : 1;
+  a.pages_per_seq = pg ? pg->pages_per_seq : 0;
+  a.num_pages = pg ? pg->num_pages : 0;
+  a.Lmax = s.Lmax;
+  a.window = s.window;
+  a.K = s.K;
+  a.per_seq = s.Lmax * s.top_k;  // the virtual list never exceeds top_k * L
   a.B = s.B;
   a.seq_rows = pg ? 0 : s.Lmax;
   a.Hq = s.Hq;

@@ -708,20 +708,14 @@ int focus_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
 }
 
 // ============================================================================ decode
-// Per-sequence plan (12 ints), each sequence's resolved key list (at most top_k * Lmax
-// entries), and the split partials (O and (max, sum) per query head and split).
+// The split partials: O and (max, sum) per query head and piece of each sequence's key list.
 struct DecodeWs {
-  int32_t* info;
-  int32_t* list;
   float* part_o;
   float* part_ml;
 };
-size_t decode_carve(void* ws, int B, int64_t Lmax, int Hq, int d_head, int top_k, int splits,
-                    DecodeWs* out) {
+size_t decode_carve(void* ws, int B, int Hq, int d_head, int splits, DecodeWs* out) {
   Carver c(ws);
   DecodeWs w{};
-  w.info = c.take<int32_t>((size_t)B * 12);
-  w.list = c.take<int32_t>((size_t)B * Lmax * top_k);
   w.part_o = c.take<float>((size_t)B * Hq * splits * d_head);
   w.part_ml = c.take<float>((size_t)B * Hq * splits * 2);
   if (out) *out = w;
@@ -738,7 +732,7 @@ size_t focus_decode_workspace_size(int B, int64_t Lmax, int Hq, int Hkv, int d_h
   s.Hkv = Hkv;
   s.G = Hq / Hkv;
   s.dh = d_head;
-  return decode_carve(nullptr, B, Lmax, Hq, d_head, top_k, decode_splits(s), nullptr);
+  return decode_carve(nullptr, B, Hq, d_head, decode_splits(s), nullptr);
 }
 
 
@@ -758,10 +752,10 @@ int focus_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_c
   const size_t need = focus_decode_workspace_size(B, Lmax, Hq, Hkv, d_head, K, top_k);
   if (!workspace || workspace_bytes < need) return FOCUS_ERR_WORKSPACE;
   DecodeWs w;
-  decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  decode_carve(workspace, B, Hq, d_head, s.splits, &w);
   return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
-                                  cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
-                                  w.part_ml, out, lse, (hipStream_t)stream));
+                                  cache_offsets, cache_idx, s, w.part_o, w.part_ml, out, lse,
+                                  (hipStream_t)stream));
 }
 
 size_t focus_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
@@ -785,10 +779,10 @@ int focus_decode_noalloc(const uint16_t* q, const int32_t* q_groups, const uint1
   void* ws = device_scratch();
   if (!ws) return FOCUS_ERR_HIP;
   DecodeWs w;
-  decode_carve(ws, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  decode_carve(ws, B, Hq, d_head, s.splits, &w);
   return hip_status(launch_decode(q, q_groups, k_cache, v_cache, cache_len, cache_groups,
-                                  cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
-                                  w.part_ml, out, lse, (hipStream_t)stream));
+                                  cache_offsets, cache_idx, s, w.part_o, w.part_ml, out, lse,
+                                  (hipStream_t)stream));
 }
 
 int focus_decode_paged(const uint16_t* q, const int32_t* q_groups, const uint16_t* k_pages,
@@ -833,11 +827,11 @@ int focus_decode_paged(const uint16_t* q, const int32_t* q_groups, const uint16_
   s.scale = sc;
   s.splits = decode_splits(s);
   DecodeWs w;
-  decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  decode_carve(workspace, B, Hq, d_head, s.splits, &w);
   DecodePaging pg{page_table, page_size, pages_per_seq, num_pages};
   return hip_status(launch_decode(q, q_groups, k_pages, v_pages, cache_len, cache_groups,
-                                  cache_offsets, cache_idx, s, w.info, w.list, w.part_o,
-                                  w.part_ml, out, lse, (hipStream_t)stream, &pg));
+                                  cache_offsets, cache_idx, s, w.part_o, w.part_ml, out, lse,
+                                  (hipStream_t)stream, &pg));
 }
 
 int focus_slots_from_bucket(const int32_t* offsets, const int32_t* idx, int batch, int64_t Lmax,
@@ -913,11 +907,11 @@ int focus_decode_slots(const uint16_t* q, const int32_t* q_groups, const uint16_
   s.scale = sc;
   s.splits = decode_splits(s);
   DecodeWs w;
-  decode_carve(workspace, B, Lmax, Hq, d_head, top_k, s.splits, &w);
+  decode_carve(workspace, B, Hq, d_head, s.splits, &w);
   DecodePaging pg{page_table, page_size, pages_per_seq, num_pages};
   DecodeSlots sl{seg_len, group_cap};
   return hip_status(launch_decode(q, q_groups, k_pages, v_pages, cache_len, cache_groups, nullptr,
-                                  seg_pos, s, w.info, w.list, w.part_o, w.part_ml, out, lse,
+                                  seg_pos, s, w.part_o, w.part_ml, out, lse,
                                   (hipStream_t)stream, &pg, &sl));
 }
 

@@ -286,8 +286,8 @@ struct DecodeSlots {
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* cache_len, const int32_t* cache_groups,
                          const int32_t* cache_off, const int32_t* cache_idx, const DecodeShape& s,
-                         int32_t* info, int32_t* list, float* part_o, float* part_ml,
-                         uint16_t* out, float* lse, hipStream_t stream,
-                         const DecodePaging* pg = nullptr, const DecodeSlots* sl = nullptr);
+                         float* part_o, float* part_ml, uint16_t* out, float* lse,
+                         hipStream_t stream, const DecodePaging* pg = nullptr,
+                         const DecodeSlots* sl = nullptr);
 
 }  // namespace focus

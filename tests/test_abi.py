@@ -328,10 +328,12 @@ def test_decode_noalloc_validation(lib):
         assert _noalloc(lib, **{name: None}) == ARG, name
     assert _noalloc(lib, ci=MIS) == ALIGN
     assert _noalloc(lib, B=0, q=None) == OK
-    # the 64 x 65536 decode fits; twice the sequences do not
+    # the scratch holds the pieces' partials: the 64 x 65536 decode and 2048 sequences (one
+    # piece each) fit, while the partials of 4096 sequences of 32 heads do not
     ws = lib.focus_decode_workspace_size
-    assert ws(64, 65536, 32, 8, 128, 64, 2) <= cap < ws(128, 65536, 32, 8, 128, 64, 2)
-    assert _noalloc(lib, B=128, L=65536, Hq=32, Hkv=8, K=64) == -7
+    assert ws(64, 65536, 32, 8, 128, 64, 2) <= ws(2048, 65536, 32, 8, 128, 64, 2) <= cap
+    assert cap < ws(4096, 1024, 32, 8, 128, 64, 2)
+    assert _noalloc(lib, B=4096, L=1024, Hq=32, Hkv=8, K=64) == -7
 
 
 def _train_args(**over):
