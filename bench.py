@@ -493,10 +493,10 @@ def train_bench(c, lam=10.0, reps=3):
 
 
 # ------------------------------------------------------------------ decode
-def decode_bench(c, steps, warmup):
-    log(f"[bench] decode {c.name}: B={c.batch} L={c.n} Hq={c.Hq}/{c.Hkv} K={c.K} top_k={c.top_k} "
+def decode_bench(c, steps, warmup, batch=None):
+    B, L = (batch or c.batch), c.n
+    log(f"[bench] decode {c.name}: B={B} L={L} Hq={c.Hq}/{c.Hkv} K={c.K} top_k={c.top_k} "
         f"window={c.window}")
-    B, L = c.batch, c.n
     dev = torch.device("cuda:0")
     cache_groups = torch.empty((B, L, c.top_k), dtype=torch.int32, device=dev)
     for b in range(B):  # cached memberships: assignment of each sequence's mixture hidden states
@@ -532,7 +532,7 @@ def decode_bench(c, steps, warmup):
                  c.window, out=out, lse=lse)
     keys = torch.exp(lse[:, 0].double()).round().sum().item()
     kv_bytes = keys * c.Hkv * c.dh * 2 * 2
-    res = {"workload": c.name, "us_per_step": us, "allowed_keys_per_query": keys / B,
+    res = {"workload": c.name, "batch": B, "us_per_step": us, "allowed_keys_per_query": keys / B,
            "kv_GBs": kv_bytes / (us * 1e-6) / 1e9}
     res["kv_pct_hbm_peak"] = 100 * res["kv_GBs"] / PEAK_HBM_GBS
     log(f"[bench]   decode {us:.1f} us/step, {keys / B:.0f} keys/query, {res['kv_GBs']:.0f} GB/s")
@@ -727,6 +727,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--decode", action="store_true",
                     help="only the batched decode workload (prints its own JSON line)")
+    ap.add_argument("--decode-batch", type=int, default=None,
+                    help="with --decode: sequences per step in place of the workload's 64")
     ap.add_argument("--workload", default=None,
                     help="time one prefill workload only, e.g. long_n1m (prints its own JSON line)")
     ap.add_argument("--train", default=None,
@@ -743,7 +745,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.decode:
         cfg = {x.name: x for x in CONFIGS}
-        print(json.dumps(decode_bench(cfg["decode_b64_l64k"], 20, 3)), flush=True)
+        print(json.dumps(decode_bench(cfg["decode_b64_l64k"], 20, 3, args.decode_batch)),
+              flush=True)
         return
     hip = Hip()
     if args.calibrate_copy:

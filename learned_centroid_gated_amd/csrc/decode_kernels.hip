@@ -402,21 +402,53 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   }
 }
 
-// One block per (sequence, query head): the pieces' partials merged by log-sum-exp. The block's
-// threads take the pieces' (max, sum) pairs one each for the common maximum and the denominator,
-// then every output dimension's weighted sum is split over NT / DH groups of pieces (piece
-// g, g + NT / DH, ...), whose results are added in group order.
+// The pieces' partials of each (sequence, query head) merged by log-sum-exp.
+// Few pieces: one block per (sequence, head), a thread per output dimension that reads every
+// piece's (max, sum) and O, in piece order.
+constexpr int kCombineLoopMax = 16;  // pieces up to which the loop form runs
 template <int DH>
-__global__ __launch_bounds__(512) void decode_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(DH) void decode_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
                                                             int splits, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
-  constexpr int NT = 512, NGRP = NT / DH, NW = NT / kWave;
+  const int64_t bh = blockIdx.x;  // b * Hq + hq
+  const int d = threadIdx.x;
+  const float2* ml = (const float2*)part_ml + bh * splits;
+  const float* po = part_o + bh * splits * DH + d;
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s].x);
+  float den = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) {
+      const float2 m = ml[s];
+      const float w = m.x == -INFINITY ? 0.f : fast_exp2(m.x - M);
+      den += w * m.y;
+      acc += w * po[(int64_t)s * DH];
+    }
+  }
+  const float o = den > 0.f ? acc / den : 0.f;
+  __bf16 ob = to_bf16(o);
+  out[bh * DH + d] = *(uint16_t*)&ob;
+  if (d == 0) lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+}
+
+// Many pieces (small batches): one block per (sequence, head, 32 output dimensions). The block's
+// threads take the pieces' (max, sum) pairs one each for the common maximum and the denominator;
+// then 16 groups of 32 lanes split the pieces (piece g, g + 16, ...) for the weighted sums,
+// which are added in group order.
+template <int DH>
+__global__ __launch_bounds__(512) void decode_combine_wide_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NT = 512, DC = 32, NGRP = NT / DC, NW = NT / kWave;
   static_assert(kDecMaxSplits <= NT, "one piece per thread for the (max, sum) pairs");
   __shared__ float2 sml[kDecMaxSplits];
   __shared__ float red[NW];
-  __shared__ float racc[NGRP][DH];
-  const int64_t bh = blockIdx.x;  // b * Hq + hq
+  __shared__ float racc[NGRP][DC];
+  const int64_t bh = blockIdx.x / (DH / DC);  // b * Hq + hq
+  const int dc = blockIdx.x % (DH / DC);
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const float2 mine = tid < splits ? ((const float2*)part_ml)[bh * splits + tid]
                                    : make_float2(-INFINITY, 0.f);
@@ -438,7 +470,7 @@ __global__ __launch_bounds__(512) void decode_combine_kernel(const float* __rest
   float den = 0.f;
 #pragma unroll
   for (int i = 0; i < NW; ++i) den += red[i];
-  const int d = tid % DH, g = tid / DH;
+  const int dl = tid % DC, g = tid / DC, d = dc * DC + dl;
   float acc = 0.f;
   if (M != -INFINITY) {
     const float* po = part_o + bh * splits * DH + d;
@@ -449,17 +481,29 @@ __global__ __launch_bounds__(512) void decode_combine_kernel(const float* __rest
       acc += wt * po[(int64_t)s * DH];
     }
   }
-  racc[g][d] = acc;
+  racc[g][dl] = acc;
   __syncthreads();
   if (g == 0) {
-    float a = racc[0][d];
+    float a = racc[0][dl];
 #pragma unroll
-    for (int i = 1; i < NGRP; ++i) a += racc[i][d];
+    for (int i = 1; i < NGRP; ++i) a += racc[i][dl];
     const float o = den > 0.f ? a / den : 0.f;
     __bf16 ob = to_bf16(o);
     out[bh * DH + d] = *(uint16_t*)&ob;
     if (d == 0) lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
   }
+}
+
+template <int DH>
+hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int Hq, int splits,
+                          uint16_t* out, float* lse, hipStream_t stream) {
+  if (splits <= kCombineLoopMax)
+    hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3((int64_t)B * Hq), dim3(DH), 0, stream,
+                       part_o, part_ml, splits, out, lse);
+  else
+    hipLaunchKernelGGL(decode_combine_wide_kernel<DH>, dim3((int64_t)B * Hq * (DH / 32)),
+                       dim3(512), 0, stream, part_o, part_ml, splits, out, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint16_t* kc,
@@ -504,15 +548,11 @@ hipError_t launch_decode(const uint16_t* q, const int32_t* q_groups, const uint1
   if (s.dh == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int64_t)s.B * s.Hq), dim3(512), 0, stream,
-                       part_o, part_ml, s.splits, out, lse);
-  } else {
-    hipLaunchKernelGGL(decode_partial_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int64_t)s.B * s.Hq), dim3(512), 0, stream,
-                       part_o, part_ml, s.splits, out, lse);
+    return launch_combine<128>(part_o, part_ml, s.B, s.Hq, s.splits, out, lse, stream);
   }
-  return hipGetLastError();
+  hipLaunchKernelGGL(decode_partial_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return launch_combine<64>(part_o, part_ml, s.B, s.Hq, s.splits, out, lse, stream);
 }
 
 }  // namespace focus
