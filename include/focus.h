@@ -337,7 +337,8 @@ int focus_decode(const uint16_t* q, const int32_t* q_groups,
  * focus_decode_noalloc_scratch_bytes() bytes (64 MiB), held until the process ends. The call
  * allocates and frees nothing. A call whose focus_decode_workspace_size(B, Lmax, Hq, Hkv,
  * d_head, K, top_k) exceeds that size returns FOCUS_ERR_SCRATCH and enqueues nothing (the
- * 64 x 65536-token decode with 32 query heads, d_head 128 and top_k 2 needs about 51 MB).
+ * 64 x 65536-token decode with 32 query heads and d_head 128 needs about 8.5 MB; up to 2048
+ * such sequences fit).
  * The first call on a device looks up that device's copy (FOCUS_ERR_HIP if the lookup fails).
  *
  * Every call on one GPU shares that GPU's scratch, and each call rewrites what it reads, so
