@@ -314,6 +314,22 @@ def _noalloc(lib, q=P, qg=P, kc=P, vc=P, ln=P, cg=P, co=P, ci=P, B=4, L=1024, Hq
                                     window, scale, out, lse, None)
 
 
+def test_decode_pieces_follow_the_batch(lib):
+    """Decode cuts each sequence's key list into pieces so that the partial kernel gets at most
+    512 blocks (two per compute unit), at most 256 pieces per sequence. With 32 query heads in
+    8 kv groups of d_head 128 a block serves all heads of one sequence, so the partials
+    (Hq * pieces * (4 d_head + 8) bytes per sequence) fill the same workspace for every batch
+    whose pieces times sequences is 512, half of it for one sequence (256 pieces), and grow
+    with the batch past 512 sequences (one piece each)."""
+    ws = lambda B: lib.focus_decode_workspace_size(B, 65536, 32, 8, 128, 64, 2)
+    per_piece = 32 * (4 * 128 + 8)
+    for B in (2, 4, 8, 16, 64, 128, 256, 512):
+        assert ws(B) == 512 * per_piece, B
+    assert ws(1) == 256 * per_piece
+    assert ws(100) == 100 * 5 * per_piece
+    assert ws(1000) == 1000 * per_piece
+
+
 def test_decode_noalloc_validation(lib):
     """The allocation-free decode refuses what focus_decode refuses, and every call whose
     scratch would exceed the fixed array, before touching the device."""

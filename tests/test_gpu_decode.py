@@ -60,6 +60,27 @@ def test_decode_large_batch(B):
     check_attention(out, lse, o_ref, l_ref, "decode, large batch")
 
 
+@pytest.mark.parametrize("B,L,Hq,Hkv,dh,K,k,w", [
+    (2, 262144, 8, 2, 64, 64, 2, 1024),  # long caches: 128 pieces of about 135 keys per sequence
+    (520, 4096, 4, 1, 64, 2, 1, 64),     # one piece per sequence, resolved 1024 entries at a time
+])
+def test_decode_long_lists(B, L, Hq, Hkv, dh, K, k, w):
+    """Long key lists: caches of 262144 tokens, and a batch large enough that each sequence's
+    list of about 2100 keys is one piece that a block resolves in several chunks."""
+    say(f"decode long lists B={B} L={L} Hq={Hq} Hkv={Hkv} dh={dh} K={K} top_k={k} window={w}")
+    rng = np.random.default_rng(B * 7 + L)
+    t = qkv_inputs(L, Hq, Hkv, dh, index=0, salt=470 + B, lead=(B,), which="kv")
+    cache_groups = np.stack([random_groups(L, K, k, rng) for _ in range(B)])
+    q_groups = np.stack([random_groups(1, K, k, rng)[0] for _ in range(B)])
+    lens = rng.integers(L // 2, L + 1, B).astype(np.int32)
+    lens[0] = L
+    qd = qkv_inputs(1, Hq, Hkv, dh, index=0, salt=480 + B, lead=(B,), which="q")["q"][:, 0]
+    out, lse = run_decode(bf16_dev(qd), i32_dev(q_groups), bf16_dev(t["k"]), bf16_dev(t["v"]),
+                          i32_dev(lens), i32_dev(cache_groups), K, w)
+    o_ref, l_ref = decode_ref(qd, q_groups, t["k"], t["v"], lens, cache_groups, w)
+    check_attention(out, lse, o_ref, l_ref, "decode, long lists")
+
+
 def test_decode_equals_last_prefill_row_on_gpu():
     from learned_centroid_gated_amd import focus_attention, focus_bucket
     L, Hq, Hkv, dh, K, k, w = 3000, 16, 4, 128, 32, 2, 128
