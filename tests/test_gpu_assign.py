@@ -56,6 +56,10 @@ CASES = [
     # one iteration: the potentials come from the score product's fused first row step alone
     (4096, 512, 128, 64, 2, 1, 64),     # folded, 128-column tiles
     (3001, 64, 32, 256, 1, 1, 40),      # two products, 256-column tiles
+    # two products with inner size 128 over at least one 256-row tile per compute unit: the
+    # persistent score kernel with the centroids resident in LDS (ragged rows, K = 200)
+    (70001, 512, 128, 200, 2, 2, 100),
+    (66000, 512, 128, 256, 1, 1, 128),
 ]
 
 
@@ -106,7 +110,8 @@ def test_assign_crowded_scores(n, d, dg, K, top_k, iters, scaled):
 
 
 @pytest.mark.parametrize("n,d,dg,K,top_k,iters", [(3000, 512, 128, 64, 2, 3),
-                                                   (3000, 256, 32, 128, 1, 2)])
+                                                   (3000, 256, 32, 128, 1, 2),
+                                                   (66000, 512, 128, 256, 1, 2)])
 def test_assign_hidden_beyond_fp16_range(n, d, dg, K, top_k, iters):
     """Some tokens carry hidden values beyond fp16's largest finite value (65504) in three
     channels whose rows of W_g are small (large activations on channels the projection
