@@ -140,8 +140,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // by one block. Each lane holds 8 dims of its unit's query heads as bf16 pairs and reads one
 // 16-byte chunk of the key's K and V rows; the dot products are reduced across the 16 lanes
 // with row moves, and a running (max, sum, O) per head absorbs the key. A lane group keeps U
-// keys' rows in flight and loads the positions of its next U keys before absorbing the
-// current ones (three rather than four in flight measured faster on the scattered rows).
+// keys' rows in flight (three rather than four measured faster on the scattered rows), their
+// positions read from the block's resolved chunk of the list in LDS.
 template <int DH>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
   constexpr int CHK = DH / 8;          // 16-byte chunks per row: lanes per key
