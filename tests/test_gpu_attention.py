@@ -42,6 +42,8 @@ CASES = [
     (1500, 8, 8, 64, 5, 4, 33, 0.7),
     (3000, 16, 1, 64, 1024, 4, 100, 0),   # largest K and top_k, G = 16
     (2500, 16, 1, 128, 1024, 3, 0, 0),
+    (1200, 4, 4, 128, 12, 4, 50, 0),      # top-4 at d_head 128, per-element ownership test
+    (1200, 16, 4, 128, 10, 4, 64, 0),     # top-4 at d_head 128, ownership as bias rows
 ]
 
 
