@@ -307,7 +307,8 @@ int focus_soft_train_backward(const float* hidden, const float* w_g, const float
  * replaced by q_groups[b].
  *
  *   q            device, [B, Hq, d_head] bf16.
- *   q_groups     device, [B, top_k] int32.
+ *   q_groups     device, [B, top_k] int32; an id outside [0, K) matches no key and a repeated
+ *                id counts once.
  *   k_cache, v_cache   device, [B, Lmax, Hkv, d_head] bf16.
  *   cache_len    device, [B] int32, 1 <= cache_len[b] <= Lmax (values outside are clamped).
  *   cache_groups device, [B, Lmax, top_k] int32.

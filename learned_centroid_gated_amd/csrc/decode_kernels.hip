@@ -182,8 +182,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
     const int64_t lo = p - wl + 1 > 0 ? p - wl + 1 : 0;
     if (wave < a.top_k) {
       const int g = a.q_groups[(int64_t)b * a.top_k + wave];
+      bool repeat = false;  // a query group listed twice contributes its members once
+      for (int r2 = 0; r2 < wave; ++r2) repeat = repeat || a.q_groups[(int64_t)b * a.top_k + r2] == g;
       int64_t s0 = 0, s1 = 0;
-      if (g >= 0 && g < a.K) {
+      if (g >= 0 && g < a.K && !repeat) {
         if (a.seg_len) {
           int64_t n = a.seg_len[(int64_t)b * a.K + g];
           n = n < 0 ? 0 : (n > a.gcap ? a.gcap : n);

@@ -81,6 +81,24 @@ def test_decode_long_lists(B, L, Hq, Hkv, dh, K, k, w):
     check_attention(out, lse, o_ref, l_ref, "decode, long lists")
 
 
+def test_decode_query_groups_invalid_or_repeated():
+    """Query groups outside [0, K) match no key and a repeated query group counts once, as in
+    the oracle (whose rule compares ids: the caches hold only valid ones); a query with no
+    valid group sees its window and itself."""
+    B, L, Hq, Hkv, dh, K, k, w = 5, 1500, 8, 2, 128, 16, 3, 64
+    say(f"decode with invalid and repeated query groups B={B} L={L} K={K} top_k={k}")
+    rng = np.random.default_rng(61)
+    t = qkv_inputs(L, Hq, Hkv, dh, index=0, salt=461, lead=(B,), which="kv")
+    cache_groups = np.stack([random_groups(L, K, k, rng) for _ in range(B)])
+    q_groups = np.array([[-1, 3, 7], [5, 5, 9], [20, -4, 2], [-1, -1, -1], [4, 4, 4]], np.int32)
+    lens = np.array([L, L - 7, 900, 321, L], np.int32)
+    qd = qkv_inputs(1, Hq, Hkv, dh, index=0, salt=462, lead=(B,), which="q")["q"][:, 0]
+    out, lse = run_decode(bf16_dev(qd), i32_dev(q_groups), bf16_dev(t["k"]), bf16_dev(t["v"]),
+                          i32_dev(lens), i32_dev(cache_groups), K, w)
+    o_ref, l_ref = decode_ref(qd, q_groups, t["k"], t["v"], lens, cache_groups, w)
+    check_attention(out, lse, o_ref, l_ref, "decode, invalid and repeated query groups")
+
+
 def test_decode_equals_last_prefill_row_on_gpu():
     from learned_centroid_gated_amd import focus_attention, focus_bucket
     L, Hq, Hkv, dh, K, k, w = 3000, 16, 4, 128, 32, 2, 128
